@@ -1,0 +1,274 @@
+"""Benchmark of the Engram layer forward hot path on one MI355X.
+
+One step = one engram_forward (row gather -> wkv projection -> gate/residual)
+over the prefill workload: T = 8192 tokens, dim 4096, hc 4, 16 hash columns of
+head_dim 128 (K = 2048, N = 20480), bf16 tables (33.6 M rows, 8.6 GB,
+HBM-resident) and bf16 wkv, Zipf(1.1) ids, no mask. Inputs are seeded and
+synthetic and already resident in HBM when the timed region starts.
+
+Prints one JSON line. ``value`` is prefill tokens/s; ``decode_t16`` carries
+the decode workload (T = 16, MXFP8 wkv) measured cold: 16 copies of the
+weight are rotated so no step finds it in the 256 MB Infinity Cache.
+``roofline`` is the dominant kernel (the wkv GEMM, MFMA-bound) with its
+duration taken from HIP events on the launch stream inside the timed region.
+``cpu_baseline`` is the CPU oracle on a bounded sample of the same workload.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Engram forward tokens/s at dim 4096 (T=8192 prefill; T=16 decode) + % roofline"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def _source_sha(rel: str) -> str:
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def _traffic(kernel: str, src: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_sha") != _source_sha(src):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def _events_time(fn, iters, stream):
+    """Average duration (ms) of fn() over iters launches, from HIP events on
+    the stream the work is enqueued on."""
+    import torch
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
+    for i in range(iters):
+        starts[i].record(stream)
+        fn(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    return [s.elapsed_time(e) for s, e in zip(starts, ends)]
+
+
+def bench_prefill(steps, warmup):
+    import torch
+
+    from gram_memory_layer_engram_amd import engram as E
+    from gram_memory_layer_engram_amd import workloads as W
+
+    wl = W.WORKLOADS["prefill"]
+    inp = W.make_inputs(wl, "cuda")
+    stream = torch.cuda.current_stream()
+    out = torch.empty_like(inp["hidden"])
+    args = E.forward_args(inp["table"], inp["ids"], inp["w"], None, inp["hidden"], inp["q"],
+                          inp["k"], None, wl.eps, wl.clamp, out)
+    ws = torch.empty(E.forward_workspace_size(args), dtype=torch.uint8, device="cuda")
+
+    def fwd(_=0):
+        E.forward(inp["table"], inp["ids"], inp["w"], None, inp["hidden"], inp["q"], inp["k"],
+                  None, wl.eps, wl.clamp, out=out, workspace=ws)
+
+    for _ in range(warmup):
+        fwd()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fwd()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+
+    # Per-kernel durations: the same three steps engram_forward enqueues,
+    # called one by one with events around each on the launch stream.
+    rows = torch.empty((wl.T, wl.C, wl.head_dim), dtype=torch.bfloat16, device="cuda")
+    kv = torch.empty((wl.T, wl.N), dtype=torch.bfloat16, device="cuda")
+    x = rows.view(wl.T, wl.K)
+    t_lookup = _events_time(lambda i: E.lookup(inp["table"], inp["ids"], rows_out=rows), steps, stream)
+    t_wkv = _events_time(lambda i: E.wkv(x, inp["w"], kv=kv), steps, stream)
+    t_gate = _events_time(lambda i: E.gate(inp["hidden"], kv, inp["q"], inp["k"], None, wl.eps,
+                                           wl.clamp, out=out), steps, stream)
+    return wl, dt, {"lookup": t_lookup, "wkv": t_wkv, "gate": t_gate}
+
+
+def bench_decode(steps, warmup, copies=16):
+    import torch
+
+    from gram_memory_layer_engram_amd import engram as E
+    from gram_memory_layer_engram_amd import workloads as W
+
+    wl = W.WORKLOADS["decode_t16"]
+    base = W.make_inputs(wl, "cuda")
+    # cold cache: distinct weight copies (16 x 40 MiB) and per-copy activations
+    sets = []
+    for v in range(copies):
+        sets.append({
+            "w": base["w"].clone(), "w_scales": base["w_scales"].clone(),
+            "ids": torch.from_numpy(W.make_ids(wl, variant=v)).cuda(),
+            "hidden": W.make_hidden(wl, device="cuda", variant=v),
+            "mask": torch.from_numpy(W.make_mask(wl, variant=v)).cuda(),
+        })
+    out = torch.empty_like(base["hidden"])
+    args = E.forward_args(base["table"], base["ids"], base["w"], base["w_scales"], base["hidden"],
+                          base["q"], base["k"], base["mask"], wl.eps, wl.clamp, out)
+    ws = torch.empty(E.forward_workspace_size(args), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def fwd(i):
+        s = sets[i % copies]
+        E.forward(base["table"], s["ids"], s["w"], s["w_scales"], s["hidden"], base["q"], base["k"],
+                  s["mask"], wl.eps, wl.clamp, out=out, workspace=ws)
+
+    for i in range(warmup):
+        fwd(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fwd(i)
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+
+    # the GEMV alone (quantize included: that is engram_wkv), cold
+    x = torch.empty((wl.T, wl.K), dtype=torch.bfloat16, device="cuda")
+    E.lookup(base["table"], base["ids"], rows_out=x.view(wl.T, wl.C, wl.head_dim))
+    kv = torch.empty((wl.T, wl.N), dtype=torch.bfloat16, device="cuda")
+    wws = torch.empty(max(1, E.load_library().engram_wkv_workspace_size(wl.T, wl.K, wl.N, E.W_MXFP8)),
+                      dtype=torch.uint8, device="cuda")
+    t_wkv = _events_time(lambda i: E.wkv(x, sets[i % copies]["w"], sets[i % copies]["w_scales"], kv=kv,
+                                         workspace=wws), steps, stream)
+    t_fwd = _events_time(fwd, steps, stream)
+    return wl, dt, {"wkv": t_wkv, "forward": t_fwd}
+
+
+def cpu_baseline(budget_s=12.0):
+    """The oracle as it stands, on the prefill workload's first tokens in
+    512-token blocks until the time budget is used."""
+    import numpy as np
+    import torch
+
+    from gram_memory_layer_engram_amd import workloads as W
+    from oracle import engram_oracle as o
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = None
+    wl = W.WORKLOADS["prefill"]
+    T_max = 4096
+    ids = W.make_ids(wl)[:T_max]
+    uniq, inv = np.unique(ids, return_inverse=True)
+    inv = inv.reshape(ids.shape)
+    table = W.make_table(wl, "cuda")
+    sub = table[torch.from_numpy(uniq).cuda().long()].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    del table
+    torch.cuda.empty_cache()
+    w, _ = W.make_weight(wl, "cpu")
+    wb = w.view(torch.int16).numpy().view(np.uint16)
+    hidden = W.make_hidden(wl, T=T_max).view(torch.int16).numpy().view(np.uint16)
+    q, k = W.make_qk(wl)
+    qb = q.view(torch.int16).numpy().view(np.uint16)
+    kb = k.view(torch.int16).numpy().view(np.uint16)
+    done, t0 = 0, time.perf_counter()
+    while done < T_max and time.perf_counter() - t0 < budget_s:
+        blk = slice(done, done + 512)
+        o.forward(sub, inv[blk], wb, None, hidden[blk], qb, kb, None, wl.eps, wl.clamp)
+        done += 512
+    el = time.perf_counter() - t0
+    return {"value": done / el, "unit": "tokens/s", "cores": threads or len(os.sched_getaffinity(0)),
+            "kind": "oracle",
+            "sample": f"prefill workload, first {done} of {wl.T} tokens in 512-token blocks "
+                      f"(NumPy fp64 oracle, {el:.1f} s; host cpus {len(os.sched_getaffinity(0))})"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print("bench.py measures one GPU: the Engram hot path here has no multi-GPU mode "
+              "(every token is independent; see DESIGN.md for how it would shard).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    from gram_memory_layer_engram_amd import engram as E
+
+    E.load_library()
+
+    wl, dt, kt = bench_prefill(a.steps, a.warmup)
+    med = {k: statistics.median(v) for k, v in kt.items()}
+    avg = {k: statistics.fmean(v) for k, v in kt.items()}
+    flops = 2.0 * wl.T * wl.K * wl.N
+    wkv_s = avg["wkv"] * 1e-3
+    achieved = flops / wkv_s / 1e12
+    roofline = {
+        "kernel": "gemm_bf16_kernel (wkv projection, 8192 x 20480 x 2048)",
+        "bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+        "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+        "traffic": _traffic("gemm_bf16_kernel", "gram_memory_layer_engram_amd/csrc/gemm_bf16.hip"),
+    }
+    # the HBM-bound kernels of the same step, against 8 TB/s
+    lookup_bytes = wl.T * wl.C * (4 + 2 * 2 * wl.head_dim)
+    gate_bytes = wl.T * (2 * wl.hc * wl.dim + (wl.hc + 1) * wl.dim) * 2
+    kernels = {
+        "lookup_us": round(avg["lookup"] * 1e3, 2),
+        "lookup_GBs": round(lookup_bytes / (avg["lookup"] * 1e-3) / 1e9, 1),
+        "wkv_us": round(avg["wkv"] * 1e3, 2), "wkv_us_median": round(med["wkv"] * 1e3, 2),
+        "gate_us": round(avg["gate"] * 1e3, 2),
+        "gate_GBs": round(gate_bytes / (avg["gate"] * 1e-3) / 1e9, 1),
+    }
+
+    dwl, ddt, dkt = bench_decode(max(a.steps, 100), a.warmup)
+    d_wkv = statistics.fmean(dkt["wkv"]) * 1e-3
+    d_fwd = statistics.fmean(dkt["forward"]) * 1e-3
+    w_bytes = dwl.N * dwl.K + dwl.N * dwl.K // 1024
+    d_alg = w_bytes + dwl.T * dwl.C * (4 + 2 * 2 * dwl.head_dim) + dwl.T * 2 * dwl.hc * dwl.dim * 2 \
+        + 2 * dwl.hc * dwl.dim * 2 + dwl.T
+    decode = {
+        "workload": "decode T=16, dim 4096, MXFP8 wkv [20480, 2048] (40 MiB), 16 weight copies rotated",
+        "value": round(dwl.T / ddt, 1), "unit": "tokens/s", "ms_per_step": round(ddt * 1e3, 4),
+        "forward_us_events": round(d_fwd * 1e6, 2),
+        "forward_hbm_frac": round(d_alg / d_fwd / 1e9 / HBM_PEAK_GBS, 4),
+        "wkv_us": round(d_wkv * 1e6, 2),
+        "wkv_GBs": round((w_bytes + dwl.T * dwl.N * 2) / d_wkv / 1e9, 1),
+        "wkv_hbm_frac": round((w_bytes + dwl.T * dwl.N * 2) / d_wkv / 1e9 / HBM_PEAK_GBS, 4),
+    }
+
+    cpu = None if a.no_cpu_baseline else cpu_baseline()
+    line = {
+        "metric": METRIC, "value": round(wl.T / dt, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(dt * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "prefill: T=8192, dim=4096, hc=4, n_hash_cols=16, head_dim=128, "
+                               "bf16 tables 33556876 rows (HBM), bf16 wkv [20480, 2048], Zipf(1.1) ids, no mask",
+                   "global_batch": wl.T, "parallelism": "none (1 GPU)"},
+        "roofline": roofline, "kernels": kernels, "decode_t16": decode, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

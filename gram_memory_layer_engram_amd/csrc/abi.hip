@@ -1,0 +1,214 @@
+// C ABI of libengram: argument validation, workspace layout and dispatch.
+// Every entry point only enqueues work on the caller's stream.
+#include "../../include/engram.h"
+#include "common.h"
+
+#include <string.h>
+
+namespace engram {
+
+const DevInfo& dev_info() {
+  static DevInfo info[64];
+  static bool ready[64] = {false};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (!ready[dev]) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+      cus = 256;
+    info[dev].num_cus = cus;
+    ready[dev] = true;
+  }
+  return info[dev];
+}
+
+}  // namespace engram
+
+using namespace engram;
+
+namespace {
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? ENGRAM_OK : ENGRAM_EHIP; }
+
+constexpr size_t kAlign = 256;
+inline size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// MXFP8 activation staging inside a workspace: codes [T, K] then scales [T, K/32].
+size_t mx_stage_bytes(int64_t T, int32_t K) {
+  return round_up((size_t)T * K) + round_up((size_t)T * (K / 32));
+}
+
+int check_wkv(const void* x, int64_t T, int32_t K, const void* w,
+              const uint8_t* w_scales, int32_t w_format, int32_t N, void* kv) {
+  if (T < 0 || K <= 0 || N <= 0) return ENGRAM_EINVAL;
+  if (T > 0 && (!x || !w || !kv)) return ENGRAM_EINVAL;
+  if (T > 0 && (!aligned16(x) || !aligned16(w) || !aligned16(kv))) return ENGRAM_EINVAL;
+  if (T > INT32_MAX) return ENGRAM_EUNSUPPORTED;
+  if (w_format == ENGRAM_W_BF16) {
+    if (K % 8 != 0 || N % 4 != 0) return ENGRAM_EUNSUPPORTED;
+  } else if (w_format == ENGRAM_W_MXFP8) {
+    if (T > 0 && (!w_scales || ((uintptr_t)w_scales & 3u))) return ENGRAM_EINVAL;
+    if (K % 128 != 0 || N % 32 != 0) return ENGRAM_EUNSUPPORTED;
+  } else {
+    return ENGRAM_EINVAL;
+  }
+  return ENGRAM_OK;
+}
+
+// Enqueue the projection given a workspace already checked to be large enough.
+int run_wkv(const void* x, int64_t T, int32_t K, const void* w,
+            const uint8_t* w_scales, int32_t w_format, int32_t N, void* kv,
+            void* workspace, hipStream_t s) {
+  if (T == 0) return ENGRAM_OK;
+  if (w_format == ENGRAM_W_BF16)
+    return hip_status(launch_gemm_bf16(x, T, K, w, N, kv, s));
+  uint8_t* xq = (uint8_t*)workspace;
+  uint8_t* xs = xq + round_up((size_t)T * K);
+  hipError_t e = launch_mx_quantize(x, T, K, xq, xs, s);
+  if (e != hipSuccess) return ENGRAM_EHIP;
+  const bool gemv = T <= kGemvMaxT && (K / 128 + 3) / 4 <= 8;
+  e = gemv ? launch_gemv_mxfp8(xq, xs, T, K, (const uint8_t*)w, w_scales, N, kv, s)
+           : launch_gemm_mxfp8(xq, xs, T, K, (const uint8_t*)w, w_scales, N, kv, s);
+  return hip_status(e);
+}
+
+int check_gate(const void* hidden, const void* kv, const void* q, const void* k,
+               int64_t T, int32_t hc, int32_t dim, void* out) {
+  if (T < 0 || hc <= 0 || dim <= 0) return ENGRAM_EINVAL;
+  if (hc > 8 || dim % 8 != 0 || dim > 16384) return ENGRAM_EUNSUPPORTED;
+  if (T > INT32_MAX) return ENGRAM_EUNSUPPORTED;
+  if (T > 0) {
+    if (!hidden || !kv || !q || !k || !out) return ENGRAM_EINVAL;
+    if (!aligned16(hidden) || !aligned16(kv) || !aligned16(q) || !aligned16(k) || !aligned16(out))
+      return ENGRAM_EINVAL;
+  }
+  return ENGRAM_OK;
+}
+
+int check_lookup(const void* table, int64_t num_rows, int32_t head_dim,
+                 const int32_t* ids, int64_t st, int64_t sc, int64_t T,
+                 int32_t n_cols, void* rows_out) {
+  if (T < 0 || n_cols <= 0 || head_dim <= 0 || num_rows < 0 || st < 0 || sc < 0)
+    return ENGRAM_EINVAL;
+  if (head_dim % 8 != 0 || head_dim > 1024) return ENGRAM_EUNSUPPORTED;
+  if (T > 0) {
+    if (!table || !ids || !rows_out) return ENGRAM_EINVAL;
+    if (!aligned16(table) || !aligned16(rows_out) || ((uintptr_t)ids & 3u)) return ENGRAM_EINVAL;
+  }
+  return ENGRAM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int engram_abi_version(void) { return ENGRAM_ABI_VERSION; }
+
+const char* engram_status_string(int status) {
+  switch (status) {
+    case ENGRAM_OK: return "ok";
+    case ENGRAM_EINVAL: return "invalid argument";
+    case ENGRAM_EUNSUPPORTED: return "unsupported shape";
+    case ENGRAM_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+int engram_lookup(const void* table, int64_t num_rows, int32_t head_dim,
+                  const int32_t* hash_ids, int64_t ids_stride_t,
+                  int64_t ids_stride_c, int64_t T, int32_t n_cols,
+                  void* rows_out, int32_t* err_flag, void* stream) {
+  int st = check_lookup(table, num_rows, head_dim, hash_ids, ids_stride_t,
+                        ids_stride_c, T, n_cols, rows_out);
+  if (st != ENGRAM_OK || T == 0) return st;
+  return hip_status(launch_lookup(table, num_rows, head_dim, hash_ids, ids_stride_t,
+                                  ids_stride_c, T, n_cols, rows_out, err_flag,
+                                  (hipStream_t)stream));
+}
+
+int engram_mx_quantize(const void* x, int64_t T, int32_t K, uint8_t* xq,
+                       uint8_t* xs, void* stream) {
+  if (T < 0 || K <= 0) return ENGRAM_EINVAL;
+  if (K % 32 != 0) return ENGRAM_EUNSUPPORTED;
+  if (T == 0) return ENGRAM_OK;
+  if (!x || !xq || !xs || !aligned16(x) || !aligned16(xq)) return ENGRAM_EINVAL;
+  return hip_status(launch_mx_quantize(x, T, K, xq, xs, (hipStream_t)stream));
+}
+
+size_t engram_wkv_workspace_size(int64_t T, int32_t K, int32_t N,
+                                 int32_t w_format) {
+  (void)N;
+  if (T <= 0 || K <= 0) return 0;
+  return w_format == ENGRAM_W_MXFP8 ? mx_stage_bytes(T, K) : 0;
+}
+
+int engram_wkv(const void* x, int64_t T, int32_t K, const void* w,
+               const uint8_t* w_scales, int32_t w_format, int32_t N, void* kv,
+               void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_wkv(x, T, K, w, w_scales, w_format, N, kv);
+  if (st != ENGRAM_OK || T == 0) return st;
+  const size_t need = engram_wkv_workspace_size(T, K, N, w_format);
+  if (workspace_bytes < need || (need && (!workspace || ((uintptr_t)workspace % kAlign))))
+    return ENGRAM_EINVAL;
+  return run_wkv(x, T, K, w, w_scales, w_format, N, kv, workspace, (hipStream_t)stream);
+}
+
+int engram_gate(const void* hidden, const void* kv, const void* q_weight,
+                const void* k_weight, const uint8_t* token_mask, int64_t T,
+                int32_t hc, int32_t dim, float eps, float clamp, void* out,
+                float* gate_out, void* stream) {
+  int st = check_gate(hidden, kv, q_weight, k_weight, T, hc, dim, out);
+  if (st != ENGRAM_OK || T == 0) return st;
+  return hip_status(launch_gate(hidden, kv, q_weight, k_weight, token_mask, T, hc,
+                                dim, eps, clamp, out, gate_out, (hipStream_t)stream));
+}
+
+// Forward workspace: staged rows [T, K] bf16 | kv [T, N] bf16 | MXFP8 staging.
+size_t engram_forward_workspace_size(const engram_forward_args* a) {
+  if (!a || a->T <= 0 || a->n_cols <= 0 || a->head_dim <= 0 || a->hc <= 0 || a->dim <= 0)
+    return 0;
+  const int64_t K = (int64_t)a->n_cols * a->head_dim;
+  const int64_t N = (int64_t)(a->hc + 1) * a->dim;
+  size_t bytes = round_up((size_t)a->T * K * 2) + round_up((size_t)a->T * N * 2);
+  if (a->w_format == ENGRAM_W_MXFP8) bytes += mx_stage_bytes(a->T, (int32_t)K);
+  return bytes;
+}
+
+int engram_forward(const engram_forward_args* a, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (!a) return ENGRAM_EINVAL;
+  const int64_t K64 = (int64_t)a->n_cols * a->head_dim;
+  const int64_t N64 = (int64_t)(a->hc + 1) * a->dim;
+  if (K64 > INT32_MAX || N64 > INT32_MAX) return ENGRAM_EUNSUPPORTED;
+  const int32_t K = (int32_t)K64, N = (int32_t)N64;
+  int st = check_lookup(a->table, a->num_rows, a->head_dim, a->hash_ids, a->ids_stride_t,
+                        a->ids_stride_c, a->T, a->n_cols, (void*)16);
+  if (st != ENGRAM_OK) return st;
+  st = check_gate(a->hidden, (void*)16, a->q_weight, a->k_weight, a->T, a->hc, a->dim, a->out);
+  if (st != ENGRAM_OK) return st;
+  st = check_wkv((void*)16, a->T, K, a->w, a->w_scales, a->w_format, N, (void*)16);
+  if (st != ENGRAM_OK) return st;
+  if (a->T == 0) return ENGRAM_OK;
+  const size_t need = engram_forward_workspace_size(a);
+  if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign)) return ENGRAM_EINVAL;
+
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* ws = (uint8_t*)workspace;
+  void* rows = ws;
+  void* kv = ws + round_up((size_t)a->T * K * 2);
+  void* mx = (uint8_t*)kv + round_up((size_t)a->T * N * 2);
+
+  hipError_t e = launch_lookup(a->table, a->num_rows, a->head_dim, a->hash_ids,
+                               a->ids_stride_t, a->ids_stride_c, a->T, a->n_cols,
+                               rows, a->err_flag, s);
+  if (e != hipSuccess) return ENGRAM_EHIP;
+  st = run_wkv(rows, a->T, K, a->w, a->w_scales, a->w_format, N, kv, mx, s);
+  if (st != ENGRAM_OK) return st;
+  e = launch_gate(a->hidden, kv, a->q_weight, a->k_weight, a->token_mask, a->T, a->hc,
+                  a->dim, a->eps, a->clamp, a->out, a->gate_out, s);
+  return hip_status(e);
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Shared device helpers and launcher declarations of libengram (gfx950).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace engram {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// bf16 halves of a packed 32-bit word -> fp32 (exact).
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest, ties to even; NaN -> quiet NaN.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return bf16_rne(lo) | (bf16_rne(hi) << 16);
+}
+
+// Device properties the launchers need (cached per device by the ABI layer).
+struct DevInfo {
+  int num_cus;
+};
+
+const DevInfo& dev_info();
+
+// ---- launchers (each validates nothing: the ABI layer has done that) ----
+hipError_t launch_lookup(const void* table, int64_t num_rows, int head_dim,
+                         const int32_t* ids, int64_t st, int64_t sc, int64_t T,
+                         int n_cols, void* out, int32_t* err, hipStream_t s);
+
+hipError_t launch_gate(const void* hidden, const void* kv, const void* q,
+                       const void* k, const uint8_t* mask, int64_t T, int hc,
+                       int dim, float eps, float clamp, void* out,
+                       float* gate_out, hipStream_t s);
+
+hipError_t launch_mx_quantize(const void* x, int64_t T, int K, uint8_t* xq,
+                              uint8_t* xs, hipStream_t s);
+
+hipError_t launch_gemm_bf16(const void* x, int64_t T, int K, const void* w,
+                            int N, void* kv, hipStream_t s);
+
+hipError_t launch_gemm_mxfp8(const uint8_t* xq, const uint8_t* xs, int64_t T,
+                             int K, const uint8_t* w, const uint8_t* ws, int N,
+                             void* kv, hipStream_t s);
+
+hipError_t launch_gemv_mxfp8(const uint8_t* xq, const uint8_t* xs, int64_t T,
+                             int K, const uint8_t* w, const uint8_t* ws, int N,
+                             void* kv, hipStream_t s);
+
+// Largest T the decode GEMV serves; above it the tiled GEMM runs.
+constexpr int kGemvMaxT = 64;
+
+}  // namespace engram

@@ -1,0 +1,220 @@
+// Gate and residual update: out = hidden + sigmoid(signed-sqrt(d)) * value.
+//
+// Math: "vllm.models.deepseek_v41.amd.engram", _engram_gate_finish_kernel
+// (one shard) together with _engram_gate_partials_kernel, which shows the two
+// kv-side sums: sum key^2 and sum hidden*q*k*key over dim; the hidden-side
+// sum is sum hidden^2. Per token and copy h:
+//   d = dot * rsqrt(hs/dim + eps) * rsqrt(ks/dim + eps) * rsqrt(dim)
+//   g = sigmoid(sqrt(max(|d|, clamp)) carrying the sign of d, negative only
+//       when d < 0)
+//   out = bf16(hidden + g * value); masked tokens copy hidden, g = 0
+// ("vllm.models.deepseek_v4_1.common.engram", Engram.forward docstring:
+// masked positions pass through untouched).
+//
+// Layout on MI355X: one workgroup per token serves all hc copies, so the
+// value row (the last dim-wide block of the kv row) is read once per token
+// instead of once per copy. Every thread owns CH 16-byte pieces of each row;
+// the 3*hc sums are reduced inside each 64-lane wavefront with cross-lane
+// shuffles, then across wavefronts through LDS in fixed wave order, so the
+// result does not depend on scheduling.
+#include "common.h"
+
+namespace engram {
+
+namespace {
+
+__device__ __forceinline__ void unpack8(const uint4& v, float* f) {
+  f[0] = bf16lo(v.x); f[1] = bf16hi(v.x);
+  f[2] = bf16lo(v.y); f[3] = bf16hi(v.y);
+  f[4] = bf16lo(v.z); f[5] = bf16hi(v.z);
+  f[6] = bf16lo(v.w); f[7] = bf16hi(v.w);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+// HC copies, CH pieces (8 bf16 each) per thread per row, BS threads.
+template <int HC, int CH, int BS>
+__global__ __launch_bounds__(BS) void gate_kernel(
+    const uint4* __restrict__ hidden, const uint4* __restrict__ kv,
+    const uint4* __restrict__ qw, const uint4* __restrict__ kw,
+    const uint8_t* __restrict__ mask, int dim8, float inv_dim,
+    float rsqrt_dim, float eps, float clamp, uint4* __restrict__ out,
+    float* __restrict__ gate_out) {
+  constexpr int NW = BS / 64;
+  constexpr bool KEEP = HC * CH <= 16;  // keep hidden in registers
+  __shared__ float red[NW][3 * HC];
+  __shared__ float gates[HC];
+
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const uint4* hrow = hidden + t * HC * dim8;
+  const uint4* kvrow = kv + t * (HC + 1) * dim8;
+  uint4* orow = out + t * HC * dim8;
+
+  if (mask && mask[t] == 0) {
+    // Masked token: the gate is shut and the position passes through.
+#pragma unroll
+    for (int h = 0; h < HC; ++h)
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const int j = tid + c * BS;
+        if (j < dim8) orow[h * dim8 + j] = hrow[h * dim8 + j];
+      }
+    if (gate_out && tid < HC) gate_out[t * HC + tid] = 0.0f;
+    return;
+  }
+
+  float hs[HC], ks[HC], dt[HC];
+#pragma unroll
+  for (int h = 0; h < HC; ++h) hs[h] = ks[h] = dt[h] = 0.0f;
+
+  uint4 hreg[KEEP ? HC : 1][CH];
+  uint4 vreg[CH];
+#pragma unroll
+  for (int c = 0; c < CH; ++c) {
+    const int j = tid + c * BS;
+    vreg[c] = j < dim8 ? kvrow[HC * dim8 + j] : make_uint4(0, 0, 0, 0);
+  }
+
+#pragma unroll
+  for (int h = 0; h < HC; ++h) {
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int j = tid + c * BS;
+      if (j < dim8) {
+        const uint4 hv = hrow[h * dim8 + j];
+        const uint4 kv8 = kvrow[h * dim8 + j];
+        const uint4 q8 = qw[h * dim8 + j];
+        const uint4 k8 = kw[h * dim8 + j];
+        if constexpr (KEEP) hreg[h][c] = hv;
+        float a[8], b[8], qf[8], kf[8];
+        unpack8(hv, a);
+        unpack8(kv8, b);
+        unpack8(q8, qf);
+        unpack8(k8, kf);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          hs[h] = fmaf(a[e], a[e], hs[h]);
+          ks[h] = fmaf(b[e], b[e], ks[h]);
+          dt[h] = fmaf(a[e] * qf[e] * kf[e], b[e], dt[h]);
+        }
+      }
+    }
+  }
+
+  const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int h = 0; h < HC; ++h) {
+    const float s0 = wave_sum(hs[h]);
+    const float s1 = wave_sum(ks[h]);
+    const float s2 = wave_sum(dt[h]);
+    if (lane == 0) {
+      red[wave][3 * h + 0] = s0;
+      red[wave][3 * h + 1] = s1;
+      red[wave][3 * h + 2] = s2;
+    }
+  }
+  __syncthreads();
+  if (tid < HC) {
+    const int h = tid;
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {  // fixed wave order
+      s0 += red[w][3 * h + 0];
+      s1 += red[w][3 * h + 1];
+      s2 += red[w][3 * h + 2];
+    }
+    const float hidden_rms = 1.0f / sqrtf(s0 * inv_dim + eps);
+    const float key_rms = 1.0f / sqrtf(s1 * inv_dim + eps);
+    const float d = s2 * hidden_rms * key_rms * rsqrt_dim;
+    float s = sqrtf(fmaxf(fabsf(d), clamp));
+    s = d < 0.0f ? -s : s;
+    const float g = 1.0f / (1.0f + expf(-s));
+    gates[h] = g;
+    if (gate_out) gate_out[t * HC + h] = g;
+  }
+  __syncthreads();
+
+#pragma unroll
+  for (int h = 0; h < HC; ++h) {
+    const float g = gates[h];
+#pragma unroll
+    for (int c = 0; c < CH; ++c) {
+      const int j = tid + c * BS;
+      if (j < dim8) {
+        uint4 hv;
+        if constexpr (KEEP) hv = hreg[h][c];
+        else hv = hrow[h * dim8 + j];
+        float a[8], v[8];
+        unpack8(hv, a);
+        unpack8(vreg[c], v);
+        uint4 o;
+        o.x = pack_bf16x2(fmaf(g, v[0], a[0]), fmaf(g, v[1], a[1]));
+        o.y = pack_bf16x2(fmaf(g, v[2], a[2]), fmaf(g, v[3], a[3]));
+        o.z = pack_bf16x2(fmaf(g, v[4], a[4]), fmaf(g, v[5], a[5]));
+        o.w = pack_bf16x2(fmaf(g, v[6], a[6]), fmaf(g, v[7], a[7]));
+        orow[h * dim8 + j] = o;
+      }
+    }
+  }
+}
+
+template <int HC, int CH, int BS>
+hipError_t launch_t(const void* hidden, const void* kv, const void* q,
+                    const void* k, const uint8_t* mask, int64_t T, int dim,
+                    float eps, float clamp, void* out, float* gate_out,
+                    hipStream_t s) {
+  hipLaunchKernelGGL((gate_kernel<HC, CH, BS>), dim3((unsigned)T), dim3(BS), 0, s,
+                     (const uint4*)hidden, (const uint4*)kv, (const uint4*)q,
+                     (const uint4*)k, mask, dim / 8, 1.0f / (float)dim,
+                     1.0f / sqrtf((float)dim), eps, clamp, (uint4*)out,
+                     gate_out);
+  return hipGetLastError();
+}
+
+template <int HC>
+hipError_t launch_hc(const void* hidden, const void* kv, const void* q,
+                     const void* k, const uint8_t* mask, int64_t T, int dim,
+                     float eps, float clamp, void* out, float* gate_out,
+                     hipStream_t s) {
+  const int dim8 = dim / 8;
+  if (dim8 <= 64) return launch_t<HC, 1, 64>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
+  if (dim8 <= 128) return launch_t<HC, 1, 128>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
+  const int ch = (dim8 + 255) / 256;
+  switch (ch) {
+    case 1: return launch_t<HC, 1, 256>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
+    case 2: return launch_t<HC, 2, 256>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
+    case 3: return launch_t<HC, 3, 256>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
+    case 4: return launch_t<HC, 4, 256>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
+    case 5: return launch_t<HC, 5, 256>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
+    case 6: return launch_t<HC, 6, 256>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
+    case 7: return launch_t<HC, 7, 256>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
+    case 8: return launch_t<HC, 8, 256>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gate(const void* hidden, const void* kv, const void* q,
+                       const void* k, const uint8_t* mask, int64_t T, int hc,
+                       int dim, float eps, float clamp, void* out,
+                       float* gate_out, hipStream_t s) {
+  switch (hc) {
+    case 1: return launch_hc<1>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
+    case 2: return launch_hc<2>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
+    case 3: return launch_hc<3>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
+    case 4: return launch_hc<4>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
+    case 5: return launch_hc<5>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
+    case 6: return launch_hc<6>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
+    case 7: return launch_hc<7>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
+    case 8: return launch_hc<8>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace engram

@@ -1,0 +1,217 @@
+"""Thin ctypes binding over libengram.so.
+
+Argument marshalling only: every step runs in the HIP kernels behind the C
+ABI (``include/engram.h``). torch supplies device memory and the current HIP
+stream. There is no fallback: without the built library or a GPU every call
+raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libengram.so")
+
+ENGRAM_OK, ENGRAM_EINVAL, ENGRAM_EUNSUPPORTED, ENGRAM_EHIP = 0, 1, 2, 3
+W_BF16, W_MXFP8 = 0, 1
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+_sz = ctypes.c_size_t
+
+
+class ForwardArgs(ctypes.Structure):
+    """Mirror of ``engram_forward_args``."""
+
+    _fields_ = [
+        ("table", _vp), ("num_rows", _i64),
+        ("hash_ids", _vp), ("ids_stride_t", _i64), ("ids_stride_c", _i64),
+        ("w", _vp), ("w_scales", _vp), ("w_format", _i32),
+        ("hidden", _vp), ("q_weight", _vp), ("k_weight", _vp), ("token_mask", _vp),
+        ("T", _i64), ("hc", _i32), ("dim", _i32), ("n_cols", _i32), ("head_dim", _i32),
+        ("eps", _f32), ("clamp", _f32),
+        ("out", _vp), ("gate_out", _vp), ("err_flag", _vp),
+    ]
+
+
+EXPORTS = {
+    "engram_abi_version": (_i32, []),
+    "engram_status_string": (ctypes.c_char_p, [_i32]),
+    "engram_lookup": (_i32, [_vp, _i64, _i32, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
+    "engram_mx_quantize": (_i32, [_vp, _i64, _i32, _vp, _vp, _vp]),
+    "engram_wkv_workspace_size": (_sz, [_i64, _i32, _i32, _i32]),
+    "engram_wkv": (_i32, [_vp, _i64, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "engram_gate": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _f32, _f32, _vp, _vp, _vp]),
+    "engram_forward_workspace_size": (_sz, [ctypes.POINTER(ForwardArgs)]),
+    "engram_forward": (_i32, [ctypes.POINTER(ForwardArgs), _vp, _sz, _vp]),
+}
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libengram.so and declare its exports (no GPU needed)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built; run `python -m gram_memory_layer_engram_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in EXPORTS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+class EngramError(RuntimeError):
+    pass
+
+
+def _check(status: int) -> None:
+    if status != ENGRAM_OK:
+        msg = load_library().engram_status_string(status).decode()
+        cls = ValueError if status in (ENGRAM_EINVAL, ENGRAM_EUNSUPPORTED) else EngramError
+        raise cls(f"libengram: {msg} (status {status})")
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libengram takes device tensors only")
+    return t.data_ptr()
+
+
+def _dense(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def lookup(table: torch.Tensor, hash_ids: torch.Tensor, rows_out: torch.Tensor | None = None,
+           err_flag: torch.Tensor | None = None) -> torch.Tensor:
+    """rows[t, c, :] = table[hash_ids[t, c], :] (hash_ids may be strided)."""
+    L = load_library()
+    _dense(table, "table")
+    T, C = hash_ids.shape
+    hd = table.shape[1]
+    if hash_ids.dtype != torch.int32:
+        raise ValueError("hash_ids must be int32")
+    if rows_out is None:
+        rows_out = torch.empty((T, C, hd), dtype=table.dtype, device=table.device)
+    _dense(rows_out, "rows_out")
+    _check(L.engram_lookup(_ptr(table), table.shape[0], hd, _ptr(hash_ids),
+                           hash_ids.stride(0), hash_ids.stride(1), T, C,
+                           _ptr(rows_out), _ptr(err_flag), _stream()))
+    return rows_out
+
+
+def mx_quantize(x: torch.Tensor, xq: torch.Tensor | None = None, xs: torch.Tensor | None = None):
+    """bf16 [T, K] -> (e4m3fn codes uint8 [T, K], E8M0 bytes uint8 [T, K/32])."""
+    L = load_library()
+    _dense(x, "x")
+    T, K = x.shape
+    if xq is None:
+        xq = torch.empty((T, K), dtype=torch.uint8, device=x.device)
+    if xs is None:
+        xs = torch.empty((T, K // 32), dtype=torch.uint8, device=x.device)
+    _check(L.engram_mx_quantize(_ptr(x), T, K, _ptr(xq), _ptr(xs), _stream()))
+    return xq, xs
+
+
+def wkv(x: torch.Tensor, w: torch.Tensor, w_scales: torch.Tensor | None = None,
+        kv: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """kv = bf16(x . W^T); MXFP8 when ``w_scales`` is given (w = uint8 codes)."""
+    L = load_library()
+    _dense(x, "x")
+    _dense(w, "w")
+    T, K = x.shape
+    N = w.shape[0]
+    fmt = W_BF16 if w_scales is None else W_MXFP8
+    if w.dim() != 2 or w.shape[1] != K:
+        raise ValueError(f"w must be [N, {K}], got {tuple(w.shape)}")
+    if fmt == W_MXFP8:
+        _dense(w_scales, "w_scales")
+        if w.dtype != torch.uint8 or tuple(w_scales.shape) != (N // 32, K // 32):
+            raise ValueError("MXFP8 wkv needs uint8 codes [N, K] and scales [N/32, K/32]")
+    elif w.dtype != torch.bfloat16 or x.dtype != torch.bfloat16:
+        raise ValueError("bf16 wkv needs bf16 x and w")
+    if kv is None:
+        kv = torch.empty((T, N), dtype=torch.bfloat16, device=x.device)
+    need = L.engram_wkv_workspace_size(T, K, N, fmt)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    _check(L.engram_wkv(_ptr(x), T, K, _ptr(w), _ptr(w_scales), fmt, N, _ptr(kv),
+                        _ptr(workspace), ws_bytes, _stream()))
+    return kv
+
+
+def gate(hidden: torch.Tensor, kv: torch.Tensor, q_weight: torch.Tensor, k_weight: torch.Tensor,
+         token_mask: torch.Tensor | None = None, eps: float = 1e-6, clamp: float = 1e-6,
+         out: torch.Tensor | None = None, gate_out: torch.Tensor | None = None) -> torch.Tensor:
+    """out = hidden + sigmoid(signed-sqrt(normalized dot)) * value, masked rows copied."""
+    L = load_library()
+    for t, n in ((hidden, "hidden"), (kv, "kv"), (q_weight, "q_weight"), (k_weight, "k_weight")):
+        _dense(t, n)
+    T, hc, dim = hidden.shape
+    if out is None:
+        out = torch.empty_like(hidden)
+    _check(L.engram_gate(_ptr(hidden), _ptr(kv), _ptr(q_weight), _ptr(k_weight),
+                         _ptr(token_mask), T, hc, dim, eps, clamp, _ptr(out),
+                         _ptr(gate_out), _stream()))
+    return out
+
+
+def forward_args(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask,
+                 eps, clamp, out, gate_out=None, err_flag=None) -> ForwardArgs:
+    T, hc, dim = hidden.shape
+    a = ForwardArgs()
+    a.table = _ptr(table); a.num_rows = table.shape[0]
+    a.hash_ids = _ptr(hash_ids)
+    a.ids_stride_t = hash_ids.stride(0); a.ids_stride_c = hash_ids.stride(1)
+    a.w = _ptr(w); a.w_scales = _ptr(w_scales)
+    a.w_format = W_BF16 if w_scales is None else W_MXFP8
+    a.hidden = _ptr(hidden); a.q_weight = _ptr(q_weight); a.k_weight = _ptr(k_weight)
+    a.token_mask = _ptr(token_mask)
+    a.T = T; a.hc = hc; a.dim = dim
+    a.n_cols = hash_ids.shape[1]; a.head_dim = table.shape[1]
+    a.eps = eps; a.clamp = clamp
+    a.out = _ptr(out); a.gate_out = _ptr(gate_out); a.err_flag = _ptr(err_flag)
+    return a
+
+
+def forward_workspace_size(args: ForwardArgs) -> int:
+    return load_library().engram_forward_workspace_size(ctypes.byref(args))
+
+
+def forward(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask=None,
+            eps=1e-6, clamp=1e-6, out=None, gate_out=None, err_flag=None, workspace=None):
+    """One Engram layer forward: lookup -> (MXFP8 quantize) -> wkv -> gate."""
+    L = load_library()
+    for t, n in ((table, "table"), (w, "w"), (hidden, "hidden"),
+                 (q_weight, "q_weight"), (k_weight, "k_weight")):
+        _dense(t, n)
+    if out is None:
+        out = torch.empty_like(hidden)
+    args = forward_args(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask,
+                        eps, clamp, out, gate_out, err_flag)
+    need = L.engram_forward_workspace_size(ctypes.byref(args))
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=hidden.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    _check(L.engram_forward(ctypes.byref(args), _ptr(workspace), ws_bytes, _stream()))
+    return out

@@ -31,8 +31,9 @@ Zipf(1.1) ids: rank ~ Zipf(1.1) redrawn until rank <= p_c, then
 ``local = ((rank-1) * a_c + b_c) mod p_c`` with seeded a_c in [1, p_c),
 b_c in [0, p_c) (a bijection since p_c is prime).
 
-Seeds: ``SeedSequence([20261202, cfg_id, variant])`` spawns eight children in
-the order table, ids, W, W-scales, hidden, q, k, mask.
+Seeds: ``SeedSequence([20261202, cfg_id, variant])`` spawns children in the
+order table, ids, W, W-scales, hidden, q, k, mask, kv (a stand-alone kv input
+for exercising the gate step by itself: N(0, kv_std) bf16).
 """
 
 from __future__ import annotations
@@ -138,7 +139,7 @@ def num_rows(wl: Workload) -> int:
 
 def _seeds(wl: Workload, variant: int) -> list[int]:
     ss = np.random.SeedSequence([SEED_BASE, wl.cfg_id, variant])
-    return [int(c.generate_state(1, dtype=np.uint64)[0] & 0x7FFFFFFFFFFFFFFF) for c in ss.spawn(8)]
+    return [int(c.generate_state(1, dtype=np.uint64)[0] & 0x7FFFFFFFFFFFFFFF) for c in ss.spawn(9)]
 
 
 def _gen(device, seed):
@@ -221,6 +222,21 @@ def make_mask(wl: Workload, T: int | None = None, variant: int = 0):
     m = np.ones(T, dtype=bool)
     m[rng.permutation(T)[: int(round(wl.mask_frac * T))]] = False
     return m
+
+
+def kv_std(wl: Workload) -> float:
+    """Typical kv standard deviation of the workload's projection."""
+    if wl.w_format == "bf16":
+        return 0.02 * 0.02 * wl.K ** 0.5
+    return 0.35
+
+
+def make_kv(wl: Workload, T: int | None = None, device="cpu", variant: int = 0) -> torch.Tensor:
+    """``[T, (hc+1)*dim]`` bf16 N(0, kv_std): a gate-step input on its own."""
+    T = wl.T if T is None else T
+    g = _gen(device, _seeds(wl, variant)[8])
+    x = torch.randn((T, wl.N), generator=g, device=device, dtype=torch.float32)
+    return (x * kv_std(wl)).to(torch.bfloat16)
 
 
 def make_inputs(wl: Workload, device="cpu", variant: int = 0, table=None, weight=None):

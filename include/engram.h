@@ -1,0 +1,189 @@
+/*
+ * engram.h -- C ABI of libengram.so, the Engram layer's forward hot path on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operations follow the vLLM API pages:
+ *   [P-common]  "vllm.models.deepseek_v4_1.common.engram"
+ *   [P-rocm]    "vllm.models.deepseek_v41.amd.engram"
+ *   [P-prefetch]"vllm.models.deepseek_v41.nvidia.specialized_decode.engram.prefetch"
+ *   [P-gemv]    "vllm.models.deepseek_v41.amd.mono.attention.gemv"
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *     never allocates, frees or keeps them; every call only enqueues kernels on
+ *     `stream` (a hipStream_t passed as void*, NULL = the null stream) and
+ *     returns without synchronising.
+ *   - bf16 tensors are passed as raw 16-bit patterns (void*). Dense tensors
+ *     are row-major and contiguous; their base addresses must be 16-byte
+ *     aligned (ENGRAM_EINVAL otherwise).
+ *   - T == 0 is a valid no-op (ENGRAM_OK, nothing launched), as on [P-common]
+ *     where empty batches return before any launch.
+ *   - Argument errors are reported synchronously through the return code.
+ *     Data-dependent errors (out-of-range hash ids) are reported through an
+ *     optional device-side flag the caller reads after synchronising.
+ *   - Results are deterministic: no floating-point atomics; every reduction
+ *     runs in a fixed order.
+ */
+#ifndef ENGRAM_H
+#define ENGRAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ENGRAM_ABI_VERSION 1
+
+/* Status codes. */
+enum {
+  ENGRAM_OK = 0,
+  ENGRAM_EINVAL = 1,       /* NULL required pointer, bad size, misalignment */
+  ENGRAM_EUNSUPPORTED = 2, /* a valid shape this build has no kernel for */
+  ENGRAM_EHIP = 3          /* a HIP runtime error at launch */
+};
+
+/* wkv weight formats. */
+enum {
+  ENGRAM_W_BF16 = 0,  /* W bf16 [N, K] row-major */
+  ENGRAM_W_MXFP8 = 1  /* W e4m3fn codes [N, K] row-major + E8M0 bytes [N/32, K/32] */
+};
+
+/* Version of this ABI (ENGRAM_ABI_VERSION). */
+int engram_abi_version(void);
+
+/* Static text for a status code. */
+const char* engram_status_string(int status);
+
+/*
+ * engram_lookup -- the row gather.
+ *   [P-common] Engram.prepare_embeddings / ParallelEngramEmbedding.lookup:
+ *   ids [T, heads] -> staged rows [T, heads, head_dim] bf16.
+ *
+ *   rows_out[t, c, :] = table[hash_ids[t * ids_stride_t + c * ids_stride_c], :]
+ *
+ *   table       bf16 [num_rows, head_dim], all per-column tables back to back
+ *               (ids are GLOBAL rows: column offset already added).
+ *   hash_ids    int32, element (t, c) at hash_ids[t*ids_stride_t + c*ids_stride_c]
+ *               (strides in elements, >= 0; a layer's view of a [T, layers, C]
+ *               hash tensor is strided).
+ *   rows_out    bf16 [T, n_cols, head_dim] contiguous.
+ *   head_dim    multiple of 8 (rows move in 16-byte pieces), <= 1024.
+ *   err_flag    optional int32 device flag; an id outside [0, num_rows) yields
+ *               a zero row and sets *err_flag = 1 (never cleared by the call).
+ */
+int engram_lookup(const void* table, int64_t num_rows, int32_t head_dim,
+                  const int32_t* hash_ids, int64_t ids_stride_t,
+                  int64_t ids_stride_c, int64_t T, int32_t n_cols,
+                  void* rows_out, int32_t* err_flag, void* stream);
+
+/*
+ * engram_mx_quantize -- MXFP8 quantization of bf16 activations.
+ *   [P-prefetch] module docstring (the WKV chain quantizes its input to MXFP8)
+ *   and [P-gemv] module docstring (tokens' MXFP8 rows). The rule (not on the
+ *   pages) is the OCP MX v1.0 conversion: per token and 32-element K block,
+ *   X = floor(log2(max|x|)) - 8, scale byte = clamp(X + 127, 0, 254) (0 for an
+ *   all-zero block), code = e4m3fn(x / 2^(byte-127)) round-to-nearest-even,
+ *   saturating at +-448, sign kept.
+ *
+ *   x   bf16 [T, K];  xq  uint8 e4m3fn codes [T, K];  xs  uint8 E8M0 [T, K/32].
+ *   K   multiple of 32.
+ */
+int engram_mx_quantize(const void* x, int64_t T, int32_t K, uint8_t* xq,
+                       uint8_t* xs, void* stream);
+
+/*
+ * engram_wkv -- the wkv projection kv = bf16(x . W^T), fp32 accumulation,
+ *   round-to-nearest-even to bf16.
+ *   [P-common] Engram.__init__ / forward: bias-free linear from
+ *   n_hash_cols*head_dim (K) to dim*(hc_mult+1) (N) on the flattened staged
+ *   rows; output row [key_0 | ... | key_{hc-1} | value].
+ *   [P-gemv] module docstring: the MXFP8 weight is row-major e4m3 [N, K] with
+ *   E8M0 scales per 32x32 block [N/32, K/32].
+ *
+ *   x          bf16 [T, K] (the staged rows [T, C, head_dim] viewed flat).
+ *   w          bf16 [N, K] (ENGRAM_W_BF16) or uint8 codes [N, K] (ENGRAM_W_MXFP8).
+ *   w_scales   uint8 [N/32, K/32] for MXFP8, NULL for bf16.
+ *   kv         bf16 [T, N].
+ *   workspace  device scratch of at least engram_wkv_workspace_size() bytes
+ *              (NULL allowed when that size is 0). For MXFP8 it holds x's
+ *              MXFP8 codes and scales. 256-byte aligned.
+ *   Shapes: bf16 needs K % 8 == 0; MXFP8 needs K % 128 == 0 and N % 32 == 0.
+ */
+size_t engram_wkv_workspace_size(int64_t T, int32_t K, int32_t N,
+                                 int32_t w_format);
+int engram_wkv(const void* x, int64_t T, int32_t K, const void* w,
+               const uint8_t* w_scales, int32_t w_format, int32_t N, void* kv,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * engram_gate -- gate and residual update.
+ *   [P-rocm] _engram_gate_finish_kernel (single shard) and
+ *   _engram_gate_partials_kernel; [P-common] Engram docstring and forward.
+ *   For every token t and copy h < hc, over d < dim:
+ *     hs  = sum hidden[t,h,d]^2
+ *     ks  = sum key[t,h,d]^2                     key = kv[t, h*dim + d]
+ *     dot = sum hidden*q[h,d]*k[h,d]*key
+ *     g   = sigmoid(sign(dot) * sqrt(max(|dot'|, clamp)))
+ *           dot' = dot * rsqrt(hs/dim + eps) * rsqrt(ks/dim + eps) * rsqrt(dim)
+ *           (sign negative only when dot' < 0)
+ *     out[t,h,d] = bf16(hidden[t,h,d] + g * value[t,d])   value = kv[t, hc*dim + d]
+ *   Tokens whose mask byte is 0 pass through: out = hidden bit for bit, g = 0.
+ *
+ *   hidden      bf16 [T, hc, dim];  kv  bf16 [T, (hc+1)*dim]
+ *   q_weight    bf16 [hc, dim];     k_weight  bf16 [hc, dim]
+ *   token_mask  optional uint8 [T] (nonzero = active; NULL = all active)
+ *   out         bf16 [T, hc, dim], must not overlap hidden or kv
+ *   gate_out    optional fp32 [T, hc]
+ *   Shapes: dim % 8 == 0, dim <= 16384, 1 <= hc <= 8.
+ */
+int engram_gate(const void* hidden, const void* kv, const void* q_weight,
+                const void* k_weight, const uint8_t* token_mask, int64_t T,
+                int32_t hc, int32_t dim, float eps, float clamp, void* out,
+                float* gate_out, void* stream);
+
+/*
+ * engram_forward -- one Engram layer forward: lookup -> (MXFP8 quantize) ->
+ *   wkv -> gate, all on `stream`.
+ *   [P-common] Engram.forward: kv = wkv(embed(hash_ids).flatten(-2)), then the
+ *   fused gate over [T, hc, dim]; the staged rows and kv live in the caller's
+ *   workspace (the pages keep them as persistent buffers: Engram.staged_rows,
+ *   EngramPrefetch's per-layer kv buffers).
+ *   Field meanings are those of the calls above; K = n_cols*head_dim and
+ *   N = (hc+1)*dim.
+ */
+typedef struct engram_forward_args {
+  const void* table;       /* bf16 [num_rows, head_dim] */
+  int64_t num_rows;
+  const int32_t* hash_ids; /* int32, strided as in engram_lookup */
+  int64_t ids_stride_t;
+  int64_t ids_stride_c;
+  const void* w;           /* wkv weight, see engram_wkv */
+  const uint8_t* w_scales; /* MXFP8 only */
+  int32_t w_format;
+  const void* hidden;      /* bf16 [T, hc, dim] */
+  const void* q_weight;    /* bf16 [hc, dim] */
+  const void* k_weight;    /* bf16 [hc, dim] */
+  const uint8_t* token_mask; /* optional uint8 [T] */
+  int64_t T;
+  int32_t hc;
+  int32_t dim;
+  int32_t n_cols;
+  int32_t head_dim;
+  float eps;
+  float clamp;
+  void* out;               /* bf16 [T, hc, dim] */
+  float* gate_out;         /* optional fp32 [T, hc] */
+  int32_t* err_flag;       /* optional, see engram_lookup */
+} engram_forward_args;
+
+size_t engram_forward_workspace_size(const engram_forward_args* a);
+int engram_forward(const engram_forward_args* a, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ENGRAM_H */

@@ -1,0 +1,456 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Inputs come from the seeded generators only; expected values come from the
+oracle only. Large workloads are generated on the device and checked on a
+seeded sample of tokens (the layer is position-wise, so the oracle computes
+exactly those tokens' outputs). Tolerances (elementwise |got-ref| <= abs +
+rel*|ref|): gather and MXFP8 codes bit-exact; kv rel 1e-2 / abs 2e-2; gate
+abs 1e-3 on a shared kv; out rel 1e-2 / abs 2e-2. Stricter internal checks
+for bf16 weights: kv relative Frobenius error <= 5e-3 and >= 99.9% of kv
+within one bf16 step of the oracle.
+"""
+
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import engram_oracle as o
+from tests._util import assert_close, bits, bf16_values, from_bits, sample_tokens, u8, ulp_distance_bf16
+from gram_memory_layer_engram_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+KV_TOL = (1e-2, 2e-2)
+OUT_TOL = (1e-2, 2e-2)
+GATE_ABS = 1e-3
+SAMPLE = 192
+
+
+def _E():
+    from gram_memory_layer_engram_amd import engram as E
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    E.load_library()
+    return E
+
+
+def _say(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+_CACHE: dict = {}
+
+
+def inputs(name: str):
+    """Device inputs of a workload, cached for the session (all of them fit
+    in HBM together: about 45 GB)."""
+    if name in _CACHE:
+        return _CACHE[name]
+    wl = W.WORKLOADS[name]
+    _say(f"generating {name}")
+    share = None
+    if name.startswith("decode_"):
+        # the four decode sizes share one table and weight
+        for k, v in _CACHE.items():
+            if k.startswith("decode_"):
+                share = v
+    inp = W.make_inputs(wl, DEV, table=None if share is None else share["table"],
+                        weight=None if share is None else (share["w"], share["w_scales"]))
+    inp["wl"] = wl
+    _CACHE[name] = inp
+    return inp
+
+
+def host_rows(inp, toks):
+    """Gathered rows of the sampled tokens as the oracle sees them: the
+    oracle's own gather on the table rows those tokens reference."""
+    ids = inp["ids"].cpu().numpy()[toks]
+    uniq, inv = np.unique(ids, return_inverse=True)
+    sub_table = bits(inp["table"][torch.from_numpy(uniq).to(DEV).long()])
+    rows, err = o.gather_rows(sub_table, inv.reshape(ids.shape))
+    assert not err
+    return rows
+
+
+def oracle_forward_sample(inp, toks):
+    wl = inp["wl"]
+    ids = inp["ids"].cpu().numpy()[toks]
+    uniq, inv = np.unique(ids, return_inverse=True)
+    sub_table = bits(inp["table"][torch.from_numpy(uniq).to(DEV).long()])
+    w = bits(inp["w"]) if inp["w_scales"] is None else u8(inp["w"])
+    ws = None if inp["w_scales"] is None else u8(inp["w_scales"])
+    hidden = bits(inp["hidden"])[toks]
+    mask = None if inp["mask"] is None else inp["mask"].cpu().numpy()[toks]
+    return o.forward(sub_table, inv.reshape(ids.shape), w, ws, hidden, bits(inp["q"]),
+                     bits(inp["k"]), mask, wl.eps, wl.clamp)
+
+
+ALL = ["tiny", "mid", "prefill", "decode_t1", "decode_t4", "decode_t16", "decode_t64", "long"]
+
+
+# ------------------------------------------------------------------ lookup --
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_lookup_bit_exact(name):
+    E = _E()
+    inp = inputs(name)
+    wl = inp["wl"]
+    _say(f"lookup {name} T={wl.T}")
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    rows = E.lookup(inp["table"], inp["ids"], err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    toks = sample_tokens(wl.T, 4096 if wl.T > 4096 else wl.T, seed=1)
+    want = host_rows(inp, toks)
+    assert np.array_equal(bits(rows)[toks], want)
+
+
+def test_lookup_strided_ids_and_bad_ids():
+    E = _E()
+    inp = inputs("tiny")
+    wl = inp["wl"]
+    # a layer's view of a [T, layers, C] hash tensor
+    three = torch.zeros((wl.T, 3, wl.C), dtype=torch.int32, device=DEV)
+    three[:, 1, :] = inp["ids"]
+    view = three[:, 1, :]
+    assert view.stride() == (3 * wl.C, 1)
+    rows = E.lookup(inp["table"], view)
+    ref = E.lookup(inp["table"], inp["ids"])
+    torch.cuda.synchronize()
+    assert torch.equal(rows.view(torch.int16), ref.view(torch.int16))
+    # out-of-range ids: zero row and the flag
+    bad = inp["ids"].clone()
+    bad[3, 2] = W.num_rows(wl)
+    bad[7, 0] = -5
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    rows = E.lookup(inp["table"], bad, err_flag=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 1
+    r = bits(rows)
+    assert not r[3, 2].any() and not r[7, 0].any()
+    want, _ = o.gather_rows(bits(inp["table"]), bad.cpu().numpy())
+    assert np.array_equal(r, want)
+    # ids at both ends of the table
+    ends = inp["ids"].clone()
+    ends[0, 0] = 0
+    ends[1, 0] = W.num_rows(wl) - 1
+    rows = E.lookup(inp["table"], ends)
+    want, _ = o.gather_rows(bits(inp["table"]), ends.cpu().numpy())
+    assert np.array_equal(bits(rows), want)
+
+
+@pytest.mark.parametrize("hd", [8, 32, 64, 128, 96])
+@pytest.mark.parametrize("T", [1, 17, 65, 1000])
+def test_lookup_shapes(hd, T):
+    E = _E()
+    g = torch.Generator(device=DEV).manual_seed(hd * 1000 + T)
+    R, C = 5003, 7
+    table = torch.randn((R, hd), generator=g, device=DEV).to(torch.bfloat16)
+    ids = torch.randint(0, R, (T, C), generator=g, device=DEV, dtype=torch.int32)
+    rows = E.lookup(table, ids)
+    want, _ = o.gather_rows(bits(table), ids.cpu().numpy())
+    assert np.array_equal(bits(rows), want)
+
+
+# -------------------------------------------------------------- quantize --
+
+
+@pytest.mark.parametrize("name", ["decode_t64", "long"])
+def test_mx_quantize_bit_exact(name):
+    E = _E()
+    inp = inputs(name)
+    wl = inp["wl"]
+    T = min(wl.T, 2048)
+    rows = E.lookup(inp["table"], inp["ids"][:T].contiguous())
+    x = rows.view(T, wl.K)
+    xq, xs = E.mx_quantize(x)
+    torch.cuda.synchronize()
+    codes, sb = o.mx_quantize(bits(x))
+    assert np.array_equal(u8(xs), sb)
+    assert np.array_equal(u8(xq), codes)
+
+
+def test_mx_quantize_edge_blocks():
+    E = _E()
+    rng = np.random.default_rng(3)
+    K = 32 * 12
+    vals = []
+    vals.append(rng.standard_normal(K))
+    z = np.zeros(K); vals.append(z)                            # all-zero blocks
+    s = rng.standard_normal(K) * 1e-38; vals.append(s)          # bf16 subnormals
+    big = rng.standard_normal(K) * 1e37; vals.append(big)       # near the top
+    sat = rng.standard_normal(K); sat[::32] = 1.99; sat[1::32] = 1.0; vals.append(sat)  # 1.99 * 2^8 saturates
+    mags = o.e4m3fn_decode(np.arange(127, dtype=np.uint8))
+    ties = np.zeros(K)
+    ties[0::32] = 256.0  # fixes the block scale at 2^0 ... element values are exact midpoints
+    for b in range(K // 32):
+        ties[b * 32 + 1: b * 32 + 32] = ((mags[1:32] + mags[:31]) / 2 * (1 if b % 2 else -1))[:31]
+    vals.append(ties)
+    neg0 = -np.abs(rng.standard_normal(K)) * 1e-30; neg0[::32] = 100.0; vals.append(neg0)
+    x_bits = o.round_to_bf16(np.stack(vals))
+    x = from_bits(x_bits, DEV)
+    xq, xs = E.mx_quantize(x)
+    torch.cuda.synchronize()
+    codes, sb = o.mx_quantize(x_bits)
+    assert np.array_equal(u8(xs), sb)
+    assert np.array_equal(u8(xq), codes)
+
+
+# -------------------------------------------------------------------- wkv --
+
+
+def _kv_checks(got_bits, ref_bits, ref64, strict):
+    got = bf16_values(got_bits)
+    assert_close(got, ref64, *KV_TOL, what="kv")
+    if strict:
+        fro = np.linalg.norm(got - ref64) / np.linalg.norm(ref64)
+        assert fro <= 5e-3, fro
+        within = np.mean(ulp_distance_bf16(got_bits, ref_bits) <= 1)
+        assert within >= 0.999, within
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "prefill", "decode_t1", "decode_t4",
+                                  "decode_t16", "decode_t64", "long"])
+def test_wkv(name):
+    E = _E()
+    inp = inputs(name)
+    wl = inp["wl"]
+    _say(f"wkv {name}")
+    rows = E.lookup(inp["table"], inp["ids"])
+    x = rows.view(wl.T, wl.K)
+    kv = E.wkv(x, inp["w"], inp["w_scales"])
+    torch.cuda.synchronize()
+    toks = sample_tokens(wl.T, SAMPLE, seed=2)
+    xs = host_rows(inp, toks).reshape(len(toks), wl.K)
+    if inp["w_scales"] is None:
+        ref_bits, ref64 = o.wkv(xs, bits(inp["w"]))
+    else:
+        ref_bits, ref64 = o.wkv(xs, u8(inp["w"]), u8(inp["w_scales"]))
+    _kv_checks(bits(kv)[toks], ref_bits, ref64, strict=inp["w_scales"] is None)
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "mxfp8"])
+@pytest.mark.parametrize("T,K,N", [(1, 256, 96), (17, 384, 288), (65, 512, 544), (300, 640, 800),
+                                   (513, 1024, 320), (64, 256, 768)])
+def test_wkv_ragged_shapes(fmt, T, K, N):
+    E = _E()
+    g = torch.Generator(device=DEV).manual_seed(T * 7 + K + N)
+    x = (torch.randn((T, K), generator=g, device=DEV) * 0.5).to(torch.bfloat16)
+    if fmt == "bf16":
+        w = (torch.randn((N, K), generator=g, device=DEV) * 0.05).to(torch.bfloat16)
+        kv = E.wkv(x, w)
+        ref_bits, ref64 = o.wkv(bits(x), bits(w))
+        _kv_checks(bits(kv), ref_bits, ref64, strict=True)
+    else:
+        if K % 128:
+            pytest.skip("MXFP8 needs K % 128 == 0")
+        w = torch.randn((N, K), generator=g, device=DEV).to(torch.float8_e4m3fn).view(torch.uint8)
+        ws = (127 + torch.randint(-8, 1, (N // 32, K // 32), generator=g, device=DEV)).to(torch.uint8)
+        kv = E.wkv(x, w, ws)
+        ref_bits, ref64 = o.wkv(bits(x), u8(w), u8(ws))
+        _kv_checks(bits(kv), ref_bits, ref64, strict=False)
+
+
+@pytest.mark.parametrize("T", [16, 200])
+def test_wkv_mxfp8_block_scales_land_on_their_blocks(T):
+    """One-hot weight codes under distinct per-block scales: every output is
+    exactly 2^(S[n/32, k/32]-127) times the activation, on the GEMV (T <= 64)
+    and the GEMM path."""
+    E = _E()
+    N, K = 256, 512
+    S = ((np.arange(N // 32)[:, None] * 5 + np.arange(K // 32)[None, :] * 3) % 23 + 110).astype(np.uint8)
+    rng = np.random.default_rng(T)
+    w = np.zeros((N, K), np.uint8)
+    ks = rng.integers(0, K, size=N)
+    w[np.arange(N), ks] = 0x38  # 1.0
+    x = o.round_to_bf16(rng.standard_normal((T, K)))
+    kv = E.wkv(from_bits(x, DEV), torch.from_numpy(w).to(DEV), torch.from_numpy(S).to(DEV))
+    torch.cuda.synchronize()
+    ref_bits, ref64 = o.wkv(x, w, S)
+    assert np.array_equal(bits(kv), ref_bits)
+
+
+# ------------------------------------------------------------------- gate --
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "prefill", "decode_t1", "decode_t16", "long"])
+def test_gate_on_shared_kv(name):
+    E = _E()
+    inp = inputs(name)
+    wl = inp["wl"]
+    _say(f"gate {name}")
+    kv = W.make_kv(wl, device=DEV)
+    gate_out = torch.empty((wl.T, wl.hc), dtype=torch.float32, device=DEV)
+    out = E.gate(inp["hidden"], kv, inp["q"], inp["k"], inp["mask"], wl.eps, wl.clamp,
+                 gate_out=gate_out)
+    torch.cuda.synchronize()
+    toks = sample_tokens(wl.T, 1024, seed=3)
+    mask = None if inp["mask"] is None else inp["mask"].cpu().numpy()[toks]
+    hid = bits(inp["hidden"])[toks]
+    ref_out, ref_g = o.gate(hid, bits(kv)[toks], bits(inp["q"]), bits(inp["k"]), mask, wl.eps, wl.clamp)
+    g = gate_out.cpu().numpy().astype(np.float64)[toks]
+    assert np.max(np.abs(g - ref_g)) <= GATE_ABS
+    got = bits(out)[toks]
+    assert_close(bf16_values(got), bf16_values(ref_out), *OUT_TOL, what="out")
+    if mask is not None:
+        assert np.array_equal(got[~mask], hid[~mask])
+        assert np.all(g[~mask] == 0)
+    act = g if mask is None else g[mask]
+    assert np.all((act > 0) & (act < 1))
+
+
+@pytest.mark.parametrize("hc,dim", [(1, 8), (2, 256), (3, 520), (4, 2048), (4, 7168), (8, 1024), (2, 16384)])
+@pytest.mark.parametrize("T", [1, 2, 15, 65])
+def test_gate_shapes(hc, dim, T):
+    E = _E()
+    g = torch.Generator(device=DEV).manual_seed(hc * 100003 + dim + T)
+    hidden = torch.randn((T, hc, dim), generator=g, device=DEV).to(torch.bfloat16)
+    kv = (torch.randn((T, (hc + 1) * dim), generator=g, device=DEV) * 0.3).to(torch.bfloat16)
+    q = (1 + 0.1 * torch.randn((hc, dim), generator=g, device=DEV)).to(torch.bfloat16)
+    k = (1 + 0.1 * torch.randn((hc, dim), generator=g, device=DEV)).to(torch.bfloat16)
+    mask = torch.rand((T,), generator=g, device=DEV) > 0.3
+    gate_out = torch.empty((T, hc), dtype=torch.float32, device=DEV)
+    out = E.gate(hidden, kv, q, k, mask, 1e-6, 1e-6, gate_out=gate_out)
+    torch.cuda.synchronize()
+    ref_out, ref_g = o.gate(bits(hidden), bits(kv), bits(q), bits(k), mask.cpu().numpy(), 1e-6, 1e-6)
+    assert np.max(np.abs(gate_out.cpu().numpy() - ref_g)) <= GATE_ABS
+    assert_close(bf16_values(bits(out)), bf16_values(ref_out), *OUT_TOL, what="out")
+    # almost every output is the oracle's bf16 or one step away
+    assert np.mean(ulp_distance_bf16(bits(out), ref_out) <= 1) >= 0.999
+
+
+def test_gate_closed_form_and_sign():
+    """hidden = key = 1 (q = k = 1): g = sigma(dim^(1/4)/sqrt(1+eps)); key = -1
+    gives 1 - g; an orthogonal key gives sigma(+1e-3)."""
+    E = _E()
+    dim = 4096
+    hidden = torch.ones((3, 1, dim), device=DEV, dtype=torch.bfloat16)
+    kv = torch.zeros((3, 2 * dim), device=DEV, dtype=torch.bfloat16)
+    kv[0, :dim] = 1
+    kv[1, :dim] = -1
+    kv[2, :dim] = torch.tensor([1.0, -1.0], device=DEV).repeat(dim // 2).to(torch.bfloat16)
+    ones = torch.ones((1, dim), device=DEV, dtype=torch.bfloat16)
+    gate_out = torch.empty((3, 1), dtype=torch.float32, device=DEV)
+    E.gate(hidden, kv, ones, ones, None, 1e-6, 1e-6, gate_out=gate_out)
+    g = gate_out.cpu().numpy()[:, 0]
+    assert abs(g[0] - 0.9996646485) < 1e-6
+    assert abs(g[1] - (1 - 0.9996646485)) < 1e-6
+    assert abs(g[2] - 0.5002500000) < 1e-6
+
+
+# ---------------------------------------------------------------- forward --
+
+
+@pytest.mark.parametrize("name", ALL)
+def test_forward(name):
+    E = _E()
+    inp = inputs(name)
+    wl = inp["wl"]
+    _say(f"forward {name} T={wl.T}")
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gate_out = torch.empty((wl.T, wl.hc), dtype=torch.float32, device=DEV)
+    out = E.forward(inp["table"], inp["ids"], inp["w"], inp["w_scales"], inp["hidden"], inp["q"],
+                    inp["k"], inp["mask"], wl.eps, wl.clamp, gate_out=gate_out, err_flag=err)
+    out2 = E.forward(inp["table"], inp["ids"], inp["w"], inp["w_scales"], inp["hidden"], inp["q"],
+                     inp["k"], inp["mask"], wl.eps, wl.clamp)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    # deterministic: two runs are bitwise equal
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    toks = sample_tokens(wl.T, SAMPLE, seed=4)
+    ref = oracle_forward_sample(inp, toks)
+    got = bits(out)[toks]
+    assert_close(bf16_values(got), bf16_values(ref["out"]), *OUT_TOL, what="out")
+    hid = bits(inp["hidden"])[toks]
+    if inp["mask"] is not None:
+        m = inp["mask"].cpu().numpy()[toks]
+        assert np.array_equal(got[~m], hid[~m])
+        full_m = inp["mask"].cpu().numpy()
+        assert np.array_equal(bits(out)[~full_m], bits(inp["hidden"])[~full_m])
+    # the gate: forward's kv may differ from the oracle's by rounding ties, so
+    # compare the gate loosely here (it is checked to 1e-3 on a shared kv above)
+    g = gate_out.cpu().numpy()[toks]
+    assert np.max(np.abs(g - ref["gate"])) <= 2e-2
+
+
+def test_forward_mask_none_equals_all_true_and_empty():
+    E = _E()
+    inp = inputs("tiny")
+    wl = inp["wl"]
+    a = E.forward(inp["table"], inp["ids"], inp["w"], None, inp["hidden"], inp["q"], inp["k"], None)
+    allt = torch.ones(wl.T, dtype=torch.bool, device=DEV)
+    b = E.forward(inp["table"], inp["ids"], inp["w"], None, inp["hidden"], inp["q"], inp["k"], allt)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    # T = 0: nothing launched, nothing written
+    out = E.forward(inp["table"], inp["ids"][:0], inp["w"], None, inp["hidden"][:0], inp["q"], inp["k"], None)
+    assert out.shape == (0, wl.hc, wl.dim)
+
+
+def test_forward_zero_value_returns_hidden():
+    E = _E()
+    inp = inputs("tiny")
+    wl = inp["wl"]
+    w = inp["w"].clone()
+    w[wl.hc * wl.dim:] = 0  # value rows of W
+    out = E.forward(inp["table"], inp["ids"], w, None, inp["hidden"], inp["q"], inp["k"], None)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_values(bits(out)), bf16_values(bits(inp["hidden"])))
+
+
+def test_forward_small_hidden_engram_term_dominates():
+    """hidden ~ N(0, 0.02): the gated value is no longer hidden by the
+    output tolerance, so this checks the Engram term itself."""
+    E = _E()
+    inp = inputs("tiny")
+    wl = inp["wl"]
+    hidden = (inp["hidden"].float() * 0.02).to(torch.bfloat16)
+    out = E.forward(inp["table"], inp["ids"], inp["w"], None, hidden, inp["q"], inp["k"], inp["mask"])
+    torch.cuda.synchronize()
+    ref = o.forward(bits(inp["table"]), inp["ids"].cpu().numpy(), bits(inp["w"]), None, bits(hidden),
+                    bits(inp["q"]), bits(inp["k"]), inp["mask"].cpu().numpy(), wl.eps, wl.clamp)
+    got = bf16_values(bits(out))
+    want = bf16_values(ref["out"])
+    assert_close(got, want, 1e-2, 1e-3, what="out")
+    delta_got = got - bf16_values(bits(hidden))
+    delta_ref = want - bf16_values(bits(hidden))
+    assert np.linalg.norm(delta_got - delta_ref) <= 2e-2 * np.linalg.norm(delta_ref)
+
+
+# ------------------------------------------------------------ arg errors --
+
+
+def test_argument_errors():
+    E = _E()
+    inp = inputs("tiny")
+    wl = inp["wl"]
+    hidden = inp["hidden"]
+    kv = W.make_kv(wl, device=DEV)
+    # misaligned pointer: a view starting 2 bytes in
+    flat = hidden.view(-1)
+    mis = flat[1:1 + hidden.numel() - 8].view(-1)
+    L = E.load_library()
+    st = L.engram_gate(mis.data_ptr(), kv.data_ptr(), inp["q"].data_ptr(), inp["k"].data_ptr(), None,
+                       wl.T, wl.hc, wl.dim, 1e-6, 1e-6, hidden.data_ptr(), None, None)
+    assert st == E.ENGRAM_EINVAL
+    st = L.engram_gate(hidden.data_ptr(), kv.data_ptr(), inp["q"].data_ptr(), inp["k"].data_ptr(), None,
+                       wl.T, wl.hc, 12, 1e-6, 1e-6, hidden.data_ptr(), None, None)
+    assert st == E.ENGRAM_EUNSUPPORTED
+    st = L.engram_wkv(inp["ids"].data_ptr(), wl.T, 100, inp["w"].data_ptr(), None, E.W_MXFP8, wl.N,
+                      kv.data_ptr(), None, 0, None)
+    assert st in (E.ENGRAM_EINVAL, E.ENGRAM_EUNSUPPORTED)
+    # K % 8 != 0 is refused before any launch
+    x100 = torch.zeros((4, 100), dtype=torch.bfloat16, device=DEV)
+    w100 = torch.zeros((32, 100), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        E.wkv(x100, w100)
+    # operand shapes that disagree are refused by the binding
+    with pytest.raises(ValueError):
+        E.wkv(torch.zeros((4, 64), dtype=torch.bfloat16, device=DEV), inp["w"])
