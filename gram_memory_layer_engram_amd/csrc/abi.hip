@@ -57,6 +57,16 @@ int check_wkv(const void* x, int64_t T, int32_t K, const void* w,
   return ENGRAM_OK;
 }
 
+// MXFP8 projection from already-quantized activations: decode GEMV for small
+// T, tiled scaled-MFMA GEMM otherwise.
+hipError_t run_mx_projection(const uint8_t* xq, const uint8_t* xs, int64_t T, int32_t K,
+                             const void* w, const uint8_t* w_scales, int32_t N, void* kv,
+                             hipStream_t s) {
+  return gemv_mxfp8_supported(T, K)
+             ? launch_gemv_mxfp8(xq, xs, T, K, (const uint8_t*)w, w_scales, N, kv, s)
+             : launch_gemm_mxfp8(xq, xs, T, K, (const uint8_t*)w, w_scales, N, kv, s);
+}
+
 // Enqueue the projection given a workspace already checked to be large enough.
 int run_wkv(const void* x, int64_t T, int32_t K, const void* w,
             const uint8_t* w_scales, int32_t w_format, int32_t N, void* kv,
@@ -68,10 +78,7 @@ int run_wkv(const void* x, int64_t T, int32_t K, const void* w,
   uint8_t* xs = xq + round_up((size_t)T * K);
   hipError_t e = launch_mx_quantize(x, T, K, xq, xs, s);
   if (e != hipSuccess) return ENGRAM_EHIP;
-  const bool gemv = T <= kGemvMaxT && (K / 128 + 3) / 4 <= 8;
-  e = gemv ? launch_gemv_mxfp8(xq, xs, T, K, (const uint8_t*)w, w_scales, N, kv, s)
-           : launch_gemm_mxfp8(xq, xs, T, K, (const uint8_t*)w, w_scales, N, kv, s);
-  return hip_status(e);
+  return hip_status(run_mx_projection(xq, xs, T, K, w, w_scales, N, kv, s));
 }
 
 int check_gate(const void* hidden, const void* kv, const void* q, const void* k,
@@ -200,12 +207,29 @@ int engram_forward(const engram_forward_args* a, void* workspace,
   void* kv = ws + round_up((size_t)a->T * K * 2);
   void* mx = (uint8_t*)kv + round_up((size_t)a->T * N * 2);
 
-  hipError_t e = launch_lookup(a->table, a->num_rows, a->head_dim, a->hash_ids,
-                               a->ids_stride_t, a->ids_stride_c, a->T, a->n_cols,
-                               rows, a->err_flag, s);
-  if (e != hipSuccess) return ENGRAM_EHIP;
-  st = run_wkv(rows, a->T, K, a->w, a->w_scales, a->w_format, N, kv, mx, s);
-  if (st != ENGRAM_OK) return st;
+  hipError_t e;
+  if (a->w_format == ENGRAM_W_MXFP8 && decode_wkv_supported(a->T, K, N, a->head_dim)) {
+    // decode: gather + quantize + projection in one launch
+    e = launch_decode_wkv(a->table, a->num_rows, a->head_dim, a->hash_ids, a->ids_stride_t,
+                          a->ids_stride_c, a->n_cols, a->T, K, (const uint8_t*)a->w, a->w_scales,
+                          N, kv, a->err_flag, s);
+    if (e != hipSuccess) return ENGRAM_EHIP;
+  } else if (a->w_format == ENGRAM_W_MXFP8 && a->head_dim % 32 == 0) {
+    // the gather feeds the quantizer directly: bf16 staged rows never reach HBM
+    uint8_t* xq = (uint8_t*)mx;
+    uint8_t* xs = xq + round_up((size_t)a->T * K);
+    e = launch_gather_quantize(a->table, a->num_rows, a->head_dim, a->hash_ids, a->ids_stride_t,
+                               a->ids_stride_c, a->T, a->n_cols, xq, xs, a->err_flag, s);
+    if (e != hipSuccess) return ENGRAM_EHIP;
+    e = run_mx_projection(xq, xs, a->T, K, a->w, a->w_scales, N, kv, s);
+    if (e != hipSuccess) return ENGRAM_EHIP;
+  } else {
+    e = launch_lookup(a->table, a->num_rows, a->head_dim, a->hash_ids, a->ids_stride_t,
+                      a->ids_stride_c, a->T, a->n_cols, rows, a->err_flag, s);
+    if (e != hipSuccess) return ENGRAM_EHIP;
+    st = run_wkv(rows, a->T, K, a->w, a->w_scales, a->w_format, N, kv, mx, s);
+    if (st != ENGRAM_OK) return st;
+  }
   e = launch_gate(a->hidden, kv, a->q_weight, a->k_weight, a->token_mask, a->T, a->hc,
                   a->dim, a->eps, a->clamp, a->out, a->gate_out, s);
   return hip_status(e);

@@ -48,6 +48,12 @@ hipError_t launch_gate(const void* hidden, const void* kv, const void* q,
 hipError_t launch_mx_quantize(const void* x, int64_t T, int K, uint8_t* xq,
                               uint8_t* xs, hipStream_t s);
 
+// Row gather fused with the MXFP8 quantizer (head_dim % 32 == 0).
+hipError_t launch_gather_quantize(const void* table, int64_t num_rows, int head_dim,
+                                  const int32_t* ids, int64_t st, int64_t sc, int64_t T,
+                                  int n_cols, uint8_t* xq, uint8_t* xs, int32_t* err,
+                                  hipStream_t s);
+
 hipError_t launch_gemm_bf16(const void* x, int64_t T, int K, const void* w,
                             int N, void* kv, hipStream_t s);
 
@@ -61,5 +67,17 @@ hipError_t launch_gemv_mxfp8(const uint8_t* xq, const uint8_t* xs, int64_t T,
 
 // Largest T the decode GEMV serves; above it the tiled GEMM runs.
 constexpr int kGemvMaxT = 64;
+
+// Whether the decode GEMV takes (T, K): T <= kGemvMaxT and K small enough for
+// its per-wave register budget.
+bool gemv_mxfp8_supported(int64_t T, int K);
+
+// Decode projection with the gather and the MXFP8 quantizer fused in front
+// (T <= 32, activations rebuilt in LDS by every workgroup).
+bool decode_wkv_supported(int64_t T, int K, int N, int head_dim);
+hipError_t launch_decode_wkv(const void* table, int64_t num_rows, int head_dim,
+                             const int32_t* ids, int64_t st, int64_t sc, int n_cols, int64_t T,
+                             int K, const uint8_t* w, const uint8_t* ws, int N, void* kv,
+                             int32_t* err, hipStream_t s);
 
 }  // namespace engram

@@ -11,10 +11,11 @@
 // ("vllm.models.deepseek_v4_1.common.engram", Engram.forward docstring:
 // masked positions pass through untouched).
 //
-// Layout on MI355X: one workgroup per token serves all hc copies, so the
-// value row (the last dim-wide block of the kv row) is read once per token
-// instead of once per copy. Every thread owns CH 16-byte pieces of each row;
-// the 3*hc sums are reduced inside each 64-lane wavefront with cross-lane
+// Layout on MI355X: for large T one workgroup per token serves all hc copies,
+// so the value row (the last dim-wide block of the kv row) is read once per
+// token instead of once per copy; for small T the copies are split over
+// workgroups to keep enough of them in flight. Every thread owns CH 16-byte
+// pieces of each row; the 3*hc sums are reduced inside each 64-lane wavefront with cross-lane
 // shuffles, then across wavefronts through LDS in fixed wave order, so the
 // result does not depend on scheduling.
 #include "common.h"
@@ -36,12 +37,16 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-// HC copies, CH pieces (8 bf16 each) per thread per row, BS threads.
+// HC copies per workgroup, CH pieces (8 bf16 each) per thread per row, BS
+// threads. A token's hc_total copies are served by hc_total/HC workgroups
+// (blockIdx.y picks the group): all of them in one workgroup when T is large
+// (the value row is read once per token), one copy per workgroup when T is
+// small (more workgroups in flight; the value row then comes from L2).
 template <int HC, int CH, int BS>
 __global__ __launch_bounds__(BS) void gate_kernel(
     const uint4* __restrict__ hidden, const uint4* __restrict__ kv,
     const uint4* __restrict__ qw, const uint4* __restrict__ kw,
-    const uint8_t* __restrict__ mask, int dim8, float inv_dim,
+    const uint8_t* __restrict__ mask, int hc_total, int dim8, float inv_dim,
     float rsqrt_dim, float eps, float clamp, uint4* __restrict__ out,
     float* __restrict__ gate_out) {
   constexpr int NW = BS / 64;
@@ -50,10 +55,16 @@ __global__ __launch_bounds__(BS) void gate_kernel(
   __shared__ float gates[HC];
 
   const int64_t t = blockIdx.x;
+  const int h0 = blockIdx.y * HC;
   const int tid = threadIdx.x;
-  const uint4* hrow = hidden + t * HC * dim8;
-  const uint4* kvrow = kv + t * (HC + 1) * dim8;
-  uint4* orow = out + t * HC * dim8;
+  const uint4* hrow = hidden + (t * hc_total + h0) * dim8;
+  const uint4* kvrow = kv + t * (hc_total + 1) * dim8;
+  const uint4* vrow = kvrow + hc_total * dim8;
+  kvrow += h0 * dim8;
+  qw += h0 * dim8;
+  kw += h0 * dim8;
+  uint4* orow = out + (t * hc_total + h0) * dim8;
+  float* gout = gate_out ? gate_out + t * hc_total + h0 : nullptr;
 
   if (mask && mask[t] == 0) {
     // Masked token: the gate is shut and the position passes through.
@@ -64,7 +75,7 @@ __global__ __launch_bounds__(BS) void gate_kernel(
         const int j = tid + c * BS;
         if (j < dim8) orow[h * dim8 + j] = hrow[h * dim8 + j];
       }
-    if (gate_out && tid < HC) gate_out[t * HC + tid] = 0.0f;
+    if (gout && tid < HC) gout[tid] = 0.0f;
     return;
   }
 
@@ -77,7 +88,7 @@ __global__ __launch_bounds__(BS) void gate_kernel(
 #pragma unroll
   for (int c = 0; c < CH; ++c) {
     const int j = tid + c * BS;
-    vreg[c] = j < dim8 ? kvrow[HC * dim8 + j] : make_uint4(0, 0, 0, 0);
+    vreg[c] = j < dim8 ? vrow[j] : make_uint4(0, 0, 0, 0);
   }
 
 #pragma unroll
@@ -135,7 +146,7 @@ __global__ __launch_bounds__(BS) void gate_kernel(
     s = d < 0.0f ? -s : s;
     const float g = 1.0f / (1.0f + expf(-s));
     gates[h] = g;
-    if (gate_out) gate_out[t * HC + h] = g;
+    if (gout) gout[h] = g;
   }
   __syncthreads();
 
@@ -165,12 +176,12 @@ __global__ __launch_bounds__(BS) void gate_kernel(
 
 template <int HC, int CH, int BS>
 hipError_t launch_t(const void* hidden, const void* kv, const void* q,
-                    const void* k, const uint8_t* mask, int64_t T, int dim,
+                    const void* k, const uint8_t* mask, int64_t T, int hc_total, int dim,
                     float eps, float clamp, void* out, float* gate_out,
                     hipStream_t s) {
-  hipLaunchKernelGGL((gate_kernel<HC, CH, BS>), dim3((unsigned)T), dim3(BS), 0, s,
+  hipLaunchKernelGGL((gate_kernel<HC, CH, BS>), dim3((unsigned)T, hc_total / HC), dim3(BS), 0, s,
                      (const uint4*)hidden, (const uint4*)kv, (const uint4*)q,
-                     (const uint4*)k, mask, dim / 8, 1.0f / (float)dim,
+                     (const uint4*)k, mask, hc_total, dim / 8, 1.0f / (float)dim,
                      1.0f / sqrtf((float)dim), eps, clamp, (uint4*)out,
                      gate_out);
   return hipGetLastError();
@@ -178,22 +189,22 @@ hipError_t launch_t(const void* hidden, const void* kv, const void* q,
 
 template <int HC>
 hipError_t launch_hc(const void* hidden, const void* kv, const void* q,
-                     const void* k, const uint8_t* mask, int64_t T, int dim,
+                     const void* k, const uint8_t* mask, int64_t T, int hc_total, int dim,
                      float eps, float clamp, void* out, float* gate_out,
                      hipStream_t s) {
   const int dim8 = dim / 8;
-  if (dim8 <= 64) return launch_t<HC, 1, 64>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
-  if (dim8 <= 128) return launch_t<HC, 1, 128>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
+  if (dim8 <= 64) return launch_t<HC, 1, 64>(hidden, kv, q, k, mask, T, hc_total, dim, eps, clamp, out, gate_out, s);
+  if (dim8 <= 128) return launch_t<HC, 1, 128>(hidden, kv, q, k, mask, T, hc_total, dim, eps, clamp, out, gate_out, s);
   const int ch = (dim8 + 255) / 256;
   switch (ch) {
-    case 1: return launch_t<HC, 1, 256>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
-    case 2: return launch_t<HC, 2, 256>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
-    case 3: return launch_t<HC, 3, 256>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
-    case 4: return launch_t<HC, 4, 256>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
-    case 5: return launch_t<HC, 5, 256>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
-    case 6: return launch_t<HC, 6, 256>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
-    case 7: return launch_t<HC, 7, 256>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
-    case 8: return launch_t<HC, 8, 256>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
+    case 1: return launch_t<HC, 1, 256>(hidden, kv, q, k, mask, T, hc_total, dim, eps, clamp, out, gate_out, s);
+    case 2: return launch_t<HC, 2, 256>(hidden, kv, q, k, mask, T, hc_total, dim, eps, clamp, out, gate_out, s);
+    case 3: return launch_t<HC, 3, 256>(hidden, kv, q, k, mask, T, hc_total, dim, eps, clamp, out, gate_out, s);
+    case 4: return launch_t<HC, 4, 256>(hidden, kv, q, k, mask, T, hc_total, dim, eps, clamp, out, gate_out, s);
+    case 5: return launch_t<HC, 5, 256>(hidden, kv, q, k, mask, T, hc_total, dim, eps, clamp, out, gate_out, s);
+    case 6: return launch_t<HC, 6, 256>(hidden, kv, q, k, mask, T, hc_total, dim, eps, clamp, out, gate_out, s);
+    case 7: return launch_t<HC, 7, 256>(hidden, kv, q, k, mask, T, hc_total, dim, eps, clamp, out, gate_out, s);
+    case 8: return launch_t<HC, 8, 256>(hidden, kv, q, k, mask, T, hc_total, dim, eps, clamp, out, gate_out, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -204,15 +215,18 @@ hipError_t launch_gate(const void* hidden, const void* kv, const void* q,
                        const void* k, const uint8_t* mask, int64_t T, int hc,
                        int dim, float eps, float clamp, void* out,
                        float* gate_out, hipStream_t s) {
+  // Few tokens: one copy per workgroup, so T*hc workgroups share the work.
+  if (T * 2 < dev_info().num_cus && hc > 1)
+    return launch_hc<1>(hidden, kv, q, k, mask, T, hc, dim, eps, clamp, out, gate_out, s);
   switch (hc) {
-    case 1: return launch_hc<1>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
-    case 2: return launch_hc<2>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
-    case 3: return launch_hc<3>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
-    case 4: return launch_hc<4>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
-    case 5: return launch_hc<5>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
-    case 6: return launch_hc<6>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
-    case 7: return launch_hc<7>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
-    case 8: return launch_hc<8>(hidden, kv, q, k, mask, T, dim, eps, clamp, out, gate_out, s);
+    case 1: return launch_hc<1>(hidden, kv, q, k, mask, T, hc, dim, eps, clamp, out, gate_out, s);
+    case 2: return launch_hc<2>(hidden, kv, q, k, mask, T, hc, dim, eps, clamp, out, gate_out, s);
+    case 3: return launch_hc<3>(hidden, kv, q, k, mask, T, hc, dim, eps, clamp, out, gate_out, s);
+    case 4: return launch_hc<4>(hidden, kv, q, k, mask, T, hc, dim, eps, clamp, out, gate_out, s);
+    case 5: return launch_hc<5>(hidden, kv, q, k, mask, T, hc, dim, eps, clamp, out, gate_out, s);
+    case 6: return launch_hc<6>(hidden, kv, q, k, mask, T, hc, dim, eps, clamp, out, gate_out, s);
+    case 7: return launch_hc<7>(hidden, kv, q, k, mask, T, hc, dim, eps, clamp, out, gate_out, s);
+    case 8: return launch_hc<8>(hidden, kv, q, k, mask, T, hc, dim, eps, clamp, out, gate_out, s);
     default: return hipErrorInvalidValue;
   }
 }

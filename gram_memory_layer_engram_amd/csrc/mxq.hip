@@ -10,83 +10,79 @@
 //   byte   = clamp(X + 127, 0, 254); 0 for an all-zero block
 //   code   = e4m3fn(x * 2^(127 - byte)), nearest-even, saturating at 448,
 //            sign bit kept
-// All of it is integer work on the bf16 bit patterns plus one exact
+// The gather can be fused in front (gather_quantize_kernel): the bf16 staged
+// rows then never reach HBM. All of it is integer work on the bf16 bit patterns plus one exact
 // power-of-two multiply, so codes are reproducible bit for bit.
 #include "common.h"
+#include "mx_rule.h"
 
 namespace engram {
 
 namespace {
-
-// |v| as fp32 with v in [0, 512): e4m3fn magnitude code (0..0x7E).
-__device__ __forceinline__ uint32_t e4m3_mag_code(float v) {
-  const uint32_t u = __float_as_uint(v);
-  if (u >= 0x43e00000u) return 0x7eu;  // >= 448: saturate
-  if (u < 0x3c800000u) {               // < 2^-6: subnormal step 2^-9
-    return (uint32_t)__builtin_rintf(v * 512.0f);  // 0..8 (8 = 2^-6, code 0x08)
-  }
-  // normal: keep 3 of fp32's 23 mantissa bits, nearest-even; a carry moves
-  // into the exponent field, which the code layout absorbs.
-  const uint32_t r = u + 0x7ffffu + ((u >> 20) & 1u);
-  uint32_t code = (r >> 20) - (120u << 3);  // exponent bias 127 -> 7
-  return code > 0x7eu ? 0x7eu : code;
-}
-
-// floor(log2(a)) of a non-zero bf16 magnitude given by its 15 low bits.
-__device__ __forceinline__ int bf16_floor_log2(uint32_t mag) {
-  const int e = (int)(mag >> 7);
-  if (e > 0) return e - 127;
-  // subnormal: m * 2^-133 with 1 <= m < 128
-  return (31 - __builtin_clz(mag)) - 133;
-}
 
 __global__ __launch_bounds__(256) void mx_quantize_kernel(
     const uint4* __restrict__ x, int64_t nblocks, uint4* __restrict__ xq,
     uint8_t* __restrict__ xs) {
   const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (b >= nblocks) return;
-  uint4 in[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) in[i] = x[b * 4 + i];
-  uint32_t w[16];
+  uint32_t w[16], packed[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    w[4 * i + 0] = in[i].x; w[4 * i + 1] = in[i].y;
-    w[4 * i + 2] = in[i].z; w[4 * i + 3] = in[i].w;
+    const uint4 v = x[b * 4 + i];
+    w[4 * i + 0] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
   }
-  uint32_t amax = 0;  // bf16 magnitudes order like unsigned integers
+  const int byte = mx_block(w, packed);
+  xq[b * 2 + 0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  xq[b * 2 + 1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+  xs[b] = (uint8_t)byte;
+}
+
+// Row gather fused with the quantizer: block b of token t is 32 elements of
+// staged row c = (b*32) / head_dim, so the bf16 rows are never written.
+__global__ __launch_bounds__(256) void gather_quantize_kernel(
+    const uint4* __restrict__ table, int64_t num_rows, int head_dim,
+    const int32_t* __restrict__ ids, int64_t st, int64_t sc, int n_cols,
+    int64_t nblocks, uint4* __restrict__ xq, uint8_t* __restrict__ xs,
+    int32_t* __restrict__ err) {
+  const int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (b >= nblocks) return;
+  const int bpr = head_dim / 32;                 // blocks per staged row
+  const int64_t row = b / bpr;                   // (t, c) flattened
+  const int part = (int)(b - row * bpr);
+  const int64_t t = row / n_cols;
+  const int c = (int)(row - t * n_cols);
+  const int64_t id = ids[t * st + (int64_t)c * sc];
+  uint32_t w[16], packed[8];
+  if (id >= 0 && id < num_rows) {
+    const uint4* src = table + (id * head_dim + part * 32) / 8;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    amax = max(amax, w[i] & 0x7fffu);
-    amax = max(amax, (w[i] >> 16) & 0x7fffu);
-  }
-  int byte = 0;
-  if (amax != 0) {
-    const int X = bf16_floor_log2(amax) - 8;
-    byte = min(max(X + 127, 0), 254);
-  }
-  // 2^(127 - byte): byte <= 246 for any finite bf16 input, a normal float
-  const float inv_scale = __uint_as_float((uint32_t)(254 - byte) << 23);
-  uint32_t packed[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    uint32_t word = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = 4 * i + j;  // element index within the block
-      const uint32_t bits = (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xffffu);
-      const float mag = __uint_as_float((bits & 0x7fffu) << 16) * inv_scale;
-      const uint32_t code = e4m3_mag_code(mag) | ((bits >> 8) & 0x80u);
-      word |= code << (8 * j);
+    for (int i = 0; i < 4; ++i) {
+      const uint4 v = src[i];
+      w[4 * i + 0] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
     }
-    packed[i] = word;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) w[i] = 0u;
+    if (err) atomicOr(err, 1);
   }
+  const int byte = mx_block(w, packed);
   xq[b * 2 + 0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
   xq[b * 2 + 1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
   xs[b] = (uint8_t)byte;
 }
 
 }  // namespace
+
+hipError_t launch_gather_quantize(const void* table, int64_t num_rows, int head_dim,
+                                  const int32_t* ids, int64_t st, int64_t sc, int64_t T,
+                                  int n_cols, uint8_t* xq, uint8_t* xs, int32_t* err,
+                                  hipStream_t s) {
+  const int64_t nblocks = T * n_cols * (head_dim / 32);
+  const int grid = (int)((nblocks + 255) / 256);
+  hipLaunchKernelGGL(gather_quantize_kernel, dim3(grid), dim3(256), 0, s, (const uint4*)table,
+                     num_rows, head_dim, ids, st, sc, n_cols, nblocks, (uint4*)xq, xs, err);
+  return hipGetLastError();
+}
 
 hipError_t launch_mx_quantize(const void* x, int64_t T, int K, uint8_t* xq,
                               uint8_t* xs, hipStream_t s) {

@@ -215,3 +215,40 @@ def forward(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask
     ws_bytes = 0 if workspace is None else workspace.numel()
     _check(L.engram_forward(ctypes.byref(args), _ptr(workspace), ws_bytes, _stream()))
     return out
+
+
+class ForwardPlan:
+    """A prepared forward: arguments are marshalled once and ``run()`` is a
+    single C call (for decode loops, where per-call Python work would
+    otherwise dominate). The plan keeps its tensors alive; change their
+    contents in place between runs, not their storage."""
+
+    def __init__(self, table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask=None,
+                 eps=1e-6, clamp=1e-6, out=None, gate_out=None, err_flag=None, workspace=None,
+                 stream=None):
+        L = load_library()
+        for t, n in ((table, "table"), (w, "w"), (hidden, "hidden"),
+                     (q_weight, "q_weight"), (k_weight, "k_weight")):
+            _dense(t, n)
+        if out is None:
+            out = torch.empty_like(hidden)
+        self.out = out
+        self._keep = (table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask, gate_out,
+                      err_flag)
+        self.args = forward_args(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask,
+                                 eps, clamp, out, gate_out, err_flag)
+        need = L.engram_forward_workspace_size(ctypes.byref(self.args))
+        if workspace is None and need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=hidden.device)
+        self.workspace = workspace
+        self._ws = _ptr(workspace)
+        self._ws_bytes = 0 if workspace is None else workspace.numel()
+        self._argp = ctypes.byref(self.args)
+        self._fn = L.engram_forward
+        self._stream = (torch.cuda.current_stream() if stream is None else stream).cuda_stream
+
+    def run(self):
+        status = self._fn(self._argp, self._ws, self._ws_bytes, self._stream)
+        if status:
+            _check(status)
+        return self.out

@@ -424,6 +424,72 @@ def test_forward_small_hidden_engram_term_dominates():
     assert np.linalg.norm(delta_got - delta_ref) <= 2e-2 * np.linalg.norm(delta_ref)
 
 
+@pytest.mark.parametrize("T", [1, 5, 16, 17, 31, 32, 33, 64, 65])
+def test_forward_mxfp8_decode_paths_and_bad_ids(T):
+    """T <= 32 runs the fused gather+quantize+GEMV launch, 33..64 the separate
+    gather-quantize and GEMV, 65 the scaled-MFMA GEMM; all against the
+    oracle, with one out-of-range id (zero row + flag)."""
+    E = _E()
+    g = torch.Generator(device=DEV).manual_seed(1000 + T)
+    R, C, hd, dim, hc = 3001, 4, 128, 256, 2
+    K, N = C * hd, (hc + 1) * dim
+    table = (torch.randn((R, hd), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    ids = torch.randint(0, R, (T, C), generator=g, device=DEV, dtype=torch.int32)
+    ids[T // 2, 1] = R + 7
+    w = torch.randn((N, K), generator=g, device=DEV).to(torch.float8_e4m3fn).view(torch.uint8)
+    ws = (127 + torch.randint(-8, 1, (N // 32, K // 32), generator=g, device=DEV)).to(torch.uint8)
+    hidden = torch.randn((T, hc, dim), generator=g, device=DEV).to(torch.bfloat16)
+    q = (1 + 0.1 * torch.randn((hc, dim), generator=g, device=DEV)).to(torch.bfloat16)
+    k = (1 + 0.1 * torch.randn((hc, dim), generator=g, device=DEV)).to(torch.bfloat16)
+    mask = torch.rand((T,), generator=g, device=DEV) > 0.2
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gate_out = torch.empty((T, hc), dtype=torch.float32, device=DEV)
+    out = E.forward(table, ids, w, ws, hidden, q, k, mask, gate_out=gate_out, err_flag=err)
+    plan = E.ForwardPlan(table, ids, w, ws, hidden, q, k, mask)
+    out2 = plan.run()
+    torch.cuda.synchronize()
+    assert int(err.item()) == 1
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    ref = o.forward(bits(table), ids.cpu().numpy(), u8(w), u8(ws), bits(hidden), bits(q), bits(k),
+                    mask.cpu().numpy(), 1e-6, 1e-6)
+    assert ref["err"]
+    assert_close(bf16_values(bits(out)), bf16_values(ref["out"]), *OUT_TOL, what="out")
+    assert np.max(np.abs(gate_out.cpu().numpy() - ref["gate"])) <= 2e-2
+
+
+def test_forward_plan_graph_replay():
+    """A decode forward captured in a HIP graph replays to the eager result,
+    with eager work and synchronizations between replays."""
+    E = _E()
+    inp = inputs("decode_t16")
+    wl = inp["wl"]
+    plan = E.ForwardPlan(inp["table"], inp["ids"], inp["w"], inp["w_scales"], inp["hidden"], inp["q"],
+                         inp["k"], inp["mask"], wl.eps, wl.clamp)
+    eager = plan.run().clone()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        plan_c = E.ForwardPlan(inp["table"], inp["ids"], inp["w"], inp["w_scales"], inp["hidden"], inp["q"],
+                               inp["k"], inp["mask"], wl.eps, wl.clamp)
+        plan_c.run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        plan_g = E.ForwardPlan(inp["table"], inp["ids"], inp["w"], inp["w_scales"], inp["hidden"], inp["q"],
+                               inp["k"], inp["mask"], wl.eps, wl.clamp, workspace=plan_c.workspace,
+                               out=plan_c.out)
+        plan_g.run()
+    for i in range(4):
+        plan_c.out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(plan_c.out.view(torch.int16), eager.view(torch.int16)), i
+        _ = (inp["hidden"].float() * 2).sum().item()  # eager work between replays
+
+
 # ------------------------------------------------------------ arg errors --
 
 
