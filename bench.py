@@ -124,15 +124,13 @@ def bench_decode(steps, warmup, copies=16):
             "mask": torch.from_numpy(W.make_mask(wl, variant=v)).cuda(),
         })
     out = torch.empty_like(base["hidden"])
-    args = E.forward_args(base["table"], base["ids"], base["w"], base["w_scales"], base["hidden"],
-                          base["q"], base["k"], base["mask"], wl.eps, wl.clamp, out)
-    ws = torch.empty(E.forward_workspace_size(args), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
+    # one prepared forward per rotated set: a step is a single C call
+    plans = [E.ForwardPlan(base["table"], s["ids"], s["w"], s["w_scales"], s["hidden"], base["q"],
+                           base["k"], s["mask"], wl.eps, wl.clamp, out=out) for s in sets]
 
     def fwd(i):
-        s = sets[i % copies]
-        E.forward(base["table"], s["ids"], s["w"], s["w_scales"], s["hidden"], base["q"], base["k"],
-                  s["mask"], wl.eps, wl.clamp, out=out, workspace=ws)
+        plans[i % copies].run()
 
     for i in range(warmup):
         fwd(i)
@@ -156,8 +154,8 @@ def bench_decode(steps, warmup, copies=16):
 
 
 def cpu_baseline(budget_s=12.0):
-    """The oracle as it stands, on the prefill workload's first tokens in
-    512-token blocks until the time budget is used."""
+    """The oracle as it stands, on the prefill workload in 512-token blocks,
+    passing over the 8192 tokens again until about budget_s seconds of work."""
     import numpy as np
     import torch
 
@@ -170,8 +168,7 @@ def cpu_baseline(budget_s=12.0):
     except Exception:  # pragma: no cover
         threads = None
     wl = W.WORKLOADS["prefill"]
-    T_max = 4096
-    ids = W.make_ids(wl)[:T_max]
+    ids = W.make_ids(wl)
     uniq, inv = np.unique(ids, return_inverse=True)
     inv = inv.reshape(ids.shape)
     table = W.make_table(wl, "cuda")
@@ -180,20 +177,22 @@ def cpu_baseline(budget_s=12.0):
     torch.cuda.empty_cache()
     w, _ = W.make_weight(wl, "cpu")
     wb = w.view(torch.int16).numpy().view(np.uint16)
-    hidden = W.make_hidden(wl, T=T_max).view(torch.int16).numpy().view(np.uint16)
+    hidden = W.make_hidden(wl).view(torch.int16).numpy().view(np.uint16)
     q, k = W.make_qk(wl)
     qb = q.view(torch.int16).numpy().view(np.uint16)
     kb = k.view(torch.int16).numpy().view(np.uint16)
     done, t0 = 0, time.perf_counter()
-    while done < T_max and time.perf_counter() - t0 < budget_s:
-        blk = slice(done, done + 512)
+    while time.perf_counter() - t0 < budget_s and done < 4 * wl.T:
+        start = done % wl.T
+        blk = slice(start, start + 512)
         o.forward(sub, inv[blk], wb, None, hidden[blk], qb, kb, None, wl.eps, wl.clamp)
         done += 512
     el = time.perf_counter() - t0
     return {"value": done / el, "unit": "tokens/s", "cores": threads or len(os.sched_getaffinity(0)),
             "kind": "oracle",
-            "sample": f"prefill workload, first {done} of {wl.T} tokens in 512-token blocks "
-                      f"(NumPy fp64 oracle, {el:.1f} s; host cpus {len(os.sched_getaffinity(0))})"}
+            "sample": f"prefill workload (T=8192, dim 4096, bf16 wkv [20480, 2048]), {done} tokens "
+                      f"in 512-token blocks, NumPy fp64 oracle, {el:.1f} s; host cpus "
+                      f"{len(os.sched_getaffinity(0))}"}
 
 
 def main():
@@ -202,6 +201,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="only run a plain 512 MiB device copy (reference for the HBM byte counters)")
     a = ap.parse_args()
     if a.gpus != 1:
         print("bench.py measures one GPU: the Engram hot path here has no multi-GPU mode "
@@ -213,6 +214,16 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if a.calib_copy:
+        n = 512 << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n, "launches": 5}))
+        return
+
     from gram_memory_layer_engram_amd import engram as E
 
     E.load_library()
@@ -227,7 +238,8 @@ def main():
         "kernel": "gemm_bf16_kernel (wkv projection, 8192 x 20480 x 2048)",
         "bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
         "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-        "traffic": _traffic("gemm_bf16_kernel", "gram_memory_layer_engram_amd/csrc/gemm_bf16.hip"),
+        "traffic": _traffic("gemm_bf16_kernel", "gram_memory_layer_engram_amd/csrc/gemm.hip"),
+        "traffic_unit": "bytes per launch past L2 (rocprofv3 FETCH_SIZE x2.0 + WRITE_SIZE, copy-calibrated)",
     }
     # the HBM-bound kernels of the same step, against 8 TB/s
     lookup_bytes = wl.T * wl.C * (4 + 2 * 2 * wl.head_dim)

@@ -208,13 +208,7 @@ int engram_forward(const engram_forward_args* a, void* workspace,
   void* mx = (uint8_t*)kv + round_up((size_t)a->T * N * 2);
 
   hipError_t e;
-  if (a->w_format == ENGRAM_W_MXFP8 && decode_wkv_supported(a->T, K, N, a->head_dim)) {
-    // decode: gather + quantize + projection in one launch
-    e = launch_decode_wkv(a->table, a->num_rows, a->head_dim, a->hash_ids, a->ids_stride_t,
-                          a->ids_stride_c, a->n_cols, a->T, K, (const uint8_t*)a->w, a->w_scales,
-                          N, kv, a->err_flag, s);
-    if (e != hipSuccess) return ENGRAM_EHIP;
-  } else if (a->w_format == ENGRAM_W_MXFP8 && a->head_dim % 32 == 0) {
+  if (a->w_format == ENGRAM_W_MXFP8 && a->head_dim % 32 == 0) {
     // the gather feeds the quantizer directly: bf16 staged rows never reach HBM
     uint8_t* xq = (uint8_t*)mx;
     uint8_t* xs = xq + round_up((size_t)a->T * K);

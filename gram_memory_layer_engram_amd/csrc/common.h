@@ -72,12 +72,5 @@ constexpr int kGemvMaxT = 64;
 // its per-wave register budget.
 bool gemv_mxfp8_supported(int64_t T, int K);
 
-// Decode projection with the gather and the MXFP8 quantizer fused in front
-// (T <= 32, activations rebuilt in LDS by every workgroup).
-bool decode_wkv_supported(int64_t T, int K, int N, int head_dim);
-hipError_t launch_decode_wkv(const void* table, int64_t num_rows, int head_dim,
-                             const int32_t* ids, int64_t st, int64_t sc, int n_cols, int64_t T,
-                             int K, const uint8_t* w, const uint8_t* ws, int N, void* kv,
-                             int32_t* err, hipStream_t s);
 
 }  // namespace engram

@@ -1,6 +1,5 @@
-// The OCP MX v1.0 conversion of 32 bf16 values to MXFP8-E4M3 (shared by the
-// stand-alone quantizer and the fused decode projection). See mxq.hip for the
-// rule and why it is used.
+// The OCP MX v1.0 conversion of 32 bf16 values to MXFP8-E4M3, used by the
+// quantizer kernels in mxq.hip (which states the rule and why it is used).
 #pragma once
 
 #include "common.h"

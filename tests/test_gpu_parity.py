@@ -426,9 +426,9 @@ def test_forward_small_hidden_engram_term_dominates():
 
 @pytest.mark.parametrize("T", [1, 5, 16, 17, 31, 32, 33, 64, 65])
 def test_forward_mxfp8_decode_paths_and_bad_ids(T):
-    """T <= 32 runs the fused gather+quantize+GEMV launch, 33..64 the separate
-    gather-quantize and GEMV, 65 the scaled-MFMA GEMM; all against the
-    oracle, with one out-of-range id (zero row + flag)."""
+    """T <= 64 runs the fused gather+quantize launch and the decode GEMV, 65
+    the scaled-MFMA GEMM; all against the oracle, with one out-of-range id
+    (zero row + flag)."""
     E = _E()
     g = torch.Generator(device=DEV).manual_seed(1000 + T)
     R, C, hd, dim, hc = 3001, 4, 128, 256, 2
