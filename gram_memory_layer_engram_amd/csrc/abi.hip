@@ -45,7 +45,7 @@ int check_wkv(const void* x, int64_t T, int32_t K, const void* w,
   if (T < 0 || K <= 0 || N <= 0) return ENGRAM_EINVAL;
   if (T > 0 && (!x || !w || !kv)) return ENGRAM_EINVAL;
   if (T > 0 && (!aligned16(x) || !aligned16(w) || !aligned16(kv))) return ENGRAM_EINVAL;
-  if (T > INT32_MAX) return ENGRAM_EUNSUPPORTED;
+  if (T > INT32_MAX || K > (1 << 20)) return ENGRAM_EUNSUPPORTED;  // 32-bit buffer offsets
   if (w_format == ENGRAM_W_BF16) {
     if (K % 8 != 0 || N % 4 != 0) return ENGRAM_EUNSUPPORTED;
   } else if (w_format == ENGRAM_W_MXFP8) {

@@ -9,23 +9,35 @@
 // W[N, K], E8M0 byte per 32x32 block S[N/32, K/32]).
 //
 // MI355X design
-//  * Both operands are K-contiguous, so an operand tile is 256 rows of 128
-//    bytes per k stage (64 bf16 or 128 e4m3), i.e. 8 pieces of 16 bytes.
-//  * A = W rows (n), B = x rows (tokens): an accumulator lane then holds 4
-//    consecutive n of one token, written as one 8-byte bf16x4 store.
+//  * Both operands are K-contiguous. A = W rows (n), B = x rows (tokens): an
+//    accumulator lane then holds 4 consecutive n of one token.
 //  * Block tile 256 (n) x 256 (tokens); four waves in 2x2, each 128x128 =
-//    4x4 MFMA tiles of 32x32 (256 fp32 accumulators per lane, in AGPRs).
+//    4x4 MFMA tiles of 32x32 (256 fp32 accumulators per lane, in AGPRs). That
+//    is the largest tile one CU's register file holds, and at K = 2048 the
+//    kernel is bound by L2 -> CU operand traffic (one 256x256 tile reads 2 x
+//    256 rows per k) and by the clock the chip sustains with MFMA and that
+//    traffic both running, not by MFMA issue: the loop is paced for the
+//    address unit, not for the matrix cores.
 //  * Global -> LDS with buffer_load ... lds (16 bytes per lane, written at
 //    LDS base + lane*16): no staging registers, no ds_write, and the buffer
 //    descriptor's range check returns zeros past the last row of W or x, so
-//    ragged tiles need no branches. Two LDS stages (2 x 64 KiB); the loads of
-//    stage k+1 are issued right after the barrier that ends stage k-1 and run
-//    under stage k's MFMAs.
-//  * LDS rows are 128 B; piece p of row r sits at p ^ ((r >> 1) & 7). The DMA
-//    writes 64 consecutive pieces per instruction (8 rows), so each lane
-//    fetches the global piece that belongs at its slot.
-//  * MFMA operand fragments are double-buffered in registers: the ds_reads of
-//    sub-step kk+1 are issued before the MFMAs of sub-step kk.
+//    ragged tiles need no branches; a stage that does not exist is loaded
+//    from an offset past the range (zeros into a buffer nobody reads), which
+//    keeps the loop free of branches.
+//  * bf16: a k stage is 32 elements (64-byte LDS rows of 4 pieces, piece p of
+//    row r at p ^ ((r >> 2) & 3), conflict-free for the 32-row fragment
+//    reads). Four stages (128 KiB); the loads of stage k+3 are spread over
+//    stage k, one DMA per 4 MFMAs, so the address unit sees a steady stream
+//    instead of bursts that stall the issuing wave. The barrier that
+//    publishes stage k+1 sits after the first 4 of the last 16 MFMAs of
+//    stage k, and the next stage's first fragments are read under the other
+//    12.
+//  * MXFP8: a k stage is 128 e4m3 per row (128-byte LDS rows, piece p of row
+//    r at p ^ ((r >> 1) & 7)), two stages.
+//  * Epilogue: the bf16 tile is staged in LDS as [token][n] (512-byte rows,
+//    16-byte chunks XOR-swizzled by token) and written back as whole rows,
+//    16 bytes per lane: 8 full cache lines per store instruction instead of
+//    32 partial ones, which halves the epilogue.
 //  * Tile order is XCD-aware (workgroup ids are dealt round-robin over the 8
 //    XCDs): ids are regrouped per XCD, then walked in groups of 4 token tiles
 //    so the 32 workgroups an XCD runs at once share 4 x-tiles and 8 W-tiles
@@ -46,12 +58,21 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int BM = 256;      // W rows per block
 constexpr int BN = 256;      // tokens per block
+constexpr int THREADS = 256;
+constexpr int LDS_BYTES = 128 * 1024;            // every variant; also the epilogue's staging tile
+// MXFP8: 128-byte k stages, two of them
 constexpr int ROW_BYTES = 128;
 constexpr int PIECES = ROW_BYTES / 16;
-constexpr int THREADS = 256;
 constexpr int TILE_BYTES = BM * ROW_BYTES;       // 32 KiB
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;      // A + B
-constexpr int LDS_BYTES = 2 * STAGE_BYTES;       // two stages
+// bf16: 64-byte k stages (32 elements), four of them
+constexpr int H_ROW = 64;
+constexpr int H_TILE = BM * H_ROW;               // 16 KiB
+constexpr int H_STAGE = 2 * H_TILE;
+constexpr int H_STAGES = 4;
+constexpr int H_DMA = 8;                         // DMA instructions per wave per stage
+static_assert(H_STAGES * H_STAGE == LDS_BYTES && 2 * STAGE_BYTES == LDS_BYTES, "LDS budget");
+static_assert(BN * 512 == LDS_BYTES, "epilogue staging tile");
 constexpr int GROUP_T = 4;
 constexpr uint32_t RSRC_FLAGS = 0x00020000u;
 
@@ -82,26 +103,81 @@ __device__ __forceinline__ i32x8 cat8(const uint4& lo, const uint4& hi) {
                                  0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-// One k stage of both operand tiles, global -> LDS. Wave w issues 8 DMA
-// instructions per operand; instruction i fills rows 8*(w + 4*i) .. +8.
+// One MXFP8 k stage of both operand tiles, global -> LDS. Wave w issues 8
+// DMA instructions per operand; instruction i fills rows 8*(w + 4*i) .. +8.
 // `kb` is the stage's byte offset inside a row; `row_bytes` the global row
-// pitch; `kmax` the valid bytes of a row (pieces at or past it read zeros).
-template <bool KTAIL>
+// pitch.
 __device__ __forceinline__ void stage_load(rsrc_t ra, rsrc_t rb, char* lds_stage, int wave, int lane,
-                                           uint32_t row_bytes, uint32_t kb, uint32_t kmax) {
+                                           uint32_t row_bytes, uint32_t kb) {
   const int sub = lane >> 3, pp = lane & 7;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int blk = wave + 4 * i;
     const int r = blk * 8 + sub;
     const int p = pp ^ ((r >> 1) & 7);
-    uint32_t off = (uint32_t)r * row_bytes + kb + (uint32_t)p * 16u;
-    if (KTAIL && kb + (uint32_t)p * 16u >= kmax) off = 0xfffffff0u;  // past the range: zeros
+    const uint32_t off = (uint32_t)r * row_bytes + kb + (uint32_t)p * 16u;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(lds_stage + blk * 1024), 16, off, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(lds_stage + TILE_BYTES + blk * 1024), 16, off, 0, 0, 0);
   }
 }
 
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+// A bare workgroup barrier: unlike __syncthreads() it does not first wait
+// for every outstanding vector load, so later stages keep streaming.
+__device__ __forceinline__ void bare_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+#define SGB(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
+constexpr int SG_MFMA = 0x008, SG_VMEM = 0x010, SG_DSR = 0x100;
+
+// Write the block's accumulators to kv: stage the bf16 tile in LDS as
+// [token][n] (512-byte rows; 16-byte chunk c of row t at c ^ (t & 31)), then
+// store whole rows. The caller has drained its DMAs; LDS is free after the
+// first barrier here. Rows past T and columns past N are not written
+// (N % 4 == 0, so a row's last chunk may be half).
+__device__ __forceinline__ void store_tile(f32x16 (&acc)[4][4], char* smem, uint16_t* __restrict__ kv,
+                                           int T, int N, int t0, int n0, int wn, int wt, int lane,
+                                           int wave) {
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  wait_lgkm0();
+  bare_barrier();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int t = wt + j * 32 + lrow;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        // accumulator r of lane l: n = 8*(r/4) + 4*(l/32) + r%4, token = l%32
+        const int n = wn + i * 32 + 8 * g + 4 * lhalf;
+        uint2 o;
+        o.x = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
+        o.y = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
+        *reinterpret_cast<uint2*>(smem + t * 512 + (((n >> 3) ^ (t & 31)) << 4) + (n & 7) * 2) = o;
+      }
+  }
+  wait_lgkm0();
+  bare_barrier();
+  const int c = lane & 31;
+  const int n = n0 + c * 8;
+#pragma unroll 4
+  for (int it = 0; it < 32; ++it) {
+    const int t = wave * 64 + it * 2 + (lane >> 5);
+    const uint4 v = *reinterpret_cast<const uint4*>(smem + t * 512 + ((c ^ (t & 31)) << 4));
+    if (t0 + t < T) {
+      uint16_t* dst = kv + (int64_t)(t0 + t) * N + n;
+      if (n + 8 <= N) *reinterpret_cast<uint4*>(dst) = v;
+      else if (n + 4 <= N) *reinterpret_cast<uint2*>(dst) = make_uint2(v.x, v.y);
+    }
+  }
+}
+
+// bf16 wkv GEMM (see the file comment). KTAIL: K % 32 != 0, the last stage's
+// pieces past the row end are loaded from past the range (zeros).
 template <bool KTAIL>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_kernel(const uint16_t* __restrict__ x, int T, int K, const uint16_t* __restrict__ w,
@@ -110,12 +186,34 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ x, int T, int K, const uint16
   int tn, tt;
   tile_of(blockIdx.x, tiles_n, tiles_t, tn, tt);
   const int n0 = tn * BM, t0 = tt * BN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wn = (wave >> 1) * 128, wt = (wave & 1) * 128;
   const uint32_t row_bytes = (uint32_t)K * 2u;
   const rsrc_t ra = make_rsrc(w + (int64_t)n0 * K, (uint32_t)min(BM, N - n0) * row_bytes);
   const rsrc_t rb = make_rsrc(x + (int64_t)t0 * K, (uint32_t)min(BN, T - t0) * row_bytes);
-  const int nk = (K + 63) / 64;
+  const uint32_t oob = (uint32_t)BM * row_bytes;   // at or past both ranges
+  const int nk = (K + 31) / 32;
+
+  // DMA i of an operand (i = 0..3): LDS rows 16*(wave + 4i) .. +16, lane l
+  // fetching row 16*(wave+4i) + l/4, piece (l%4) ^ ((row >> 2) & 3).
+  uint32_t doff[4], pofs[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (wave + 4 * i) * 16 + (lane >> 2);
+    pofs[i] = (uint32_t)(((lane & 3) ^ ((r >> 2) & 3)) * 16);
+    doff[i] = (uint32_t)r * row_bytes + pofs[i];
+  }
+  // DMA j (0..7) of a stage: operand j & 1, block j >> 1; stage byte offset kofs
+  auto dma = [&](int buf, uint32_t kofs, int j) {
+    const int i = j >> 1, op = j & 1;
+    uint32_t off = doff[i] + kofs;
+    if (KTAIL && kofs + pofs[i] >= row_bytes) off = oob;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? rb : ra,
+                                             (lds_ptr_t)(smem + buf * H_STAGE + op * H_TILE +
+                                                         (wave + 4 * i) * 1024),
+                                             16, off, 0, 0, 0);
+  };
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -126,63 +224,81 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ x, int T, int K, const uint16
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   const int lrow = lane & 31, lhalf = lane >> 5;
-  stage_load<KTAIL>(ra, rb, smem, wave, lane, row_bytes, 0, row_bytes);
-  __syncthreads();
+  bf16x8_t a[2][4], b[2][4];
+  // fragment f (0..3: b0..b3, 4..7: a0..a3) of sub-step kk into register set c
+  auto frag = [&](int buf, int kk, int c, int f) {
+    const int i = f & 3;
+    const int row = (f < 4 ? wt : wn) + i * 32 + lrow;
+    const int piece = (kk * 2 + lhalf) ^ ((row >> 2) & 3);
+    const bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(smem + buf * H_STAGE + (f < 4 ? H_TILE : 0) +
+                                                          row * H_ROW + piece * 16);
+    if (f < 4) b[c][i] = v; else a[c][i] = v;
+  };
+  auto mfma_row = [&](int c, int i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
+  };
 
+  // prologue: stages 0 .. H_STAGES-2
+#pragma unroll
+  for (int s = 0; s < H_STAGES - 1; ++s)
+#pragma unroll
+    for (int j = 0; j < H_DMA; ++j) dma(s, s < nk ? (uint32_t)s * H_ROW : oob, j);
+  wait_vm<(H_STAGES - 2) * H_DMA>();
+  bare_barrier();
+#pragma unroll
+  for (int f = 0; f < 8; ++f) frag(0, 0, 0, f);
+
+  int cur = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    char* cur = smem + (kt & 1) * STAGE_BYTES;
-    if (kt + 1 < nk)
-      stage_load<KTAIL>(ra, rb, smem + ((kt + 1) & 1) * STAGE_BYTES, wave, lane, row_bytes,
-                        (uint32_t)(kt + 1) * 128u, row_bytes);
-    const uint4* As = reinterpret_cast<const uint4*>(cur);
-    const uint4* Bs = reinterpret_cast<const uint4*>(cur + TILE_BYTES);
-    bf16x8_t a[2][4], b[2][4];
+    const int nxt = cur + 1 == H_STAGES ? 0 : cur + 1;       // buffer of stage kt+1
+    const int pfb = cur == 0 ? H_STAGES - 1 : cur - 1;       // buffer of stage kt+3 (= kt-1's)
+    const uint32_t kofs = kt + H_STAGES - 1 < nk ? (uint32_t)(kt + H_STAGES - 1) * H_ROW : oob;
+    // sub-step 0: MFMAs on set 0; sub-step 1's fragments into set 1; DMAs 0-3
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      a[0][i] = __builtin_bit_cast(bf16x8_t, As[swz(wn + i * 32 + lrow, lhalf)]);
-      b[0][i] = __builtin_bit_cast(bf16x8_t, Bs[swz(wt + i * 32 + lrow, lhalf)]);
-    }
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int c = kk & 1;
-      if (kk < 3) {
-        const int piece = (kk + 1) * 2 + lhalf;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          a[c ^ 1][i] = __builtin_bit_cast(bf16x8_t, As[swz(wn + i * 32 + lrow, piece)]);
-          b[c ^ 1][i] = __builtin_bit_cast(bf16x8_t, Bs[swz(wt + i * 32 + lrow, piece)]);
-        }
-      }
-      // keep the next sub-step's LDS reads ahead of this sub-step's MFMAs
+    for (int q = 0; q < 4; ++q) {
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
+      dma(pfb, kofs, q);
+      frag(cur, 1, 1, 2 * q);
+      frag(cur, 1, 1, 2 * q + 1);
+      mfma_row(0, q);
+      SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1);
+      SGB(SG_MFMA, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1);
     }
-    __syncthreads();
-  }
-
-  // accumulator r of lane l: n = 8*(r/4) + 4*(l/32) + r%4, token = l%32
+    // sub-step 1, first quarter, then publish stage kt+1: each wave waits for
+    // its own DMAs of that stage (only the 5 issued since may still fly) and
+    // for its LDS reads of stage kt, then the barrier
+    __builtin_amdgcn_sched_barrier(0);
+    dma(pfb, kofs, 4);
+    mfma_row(1, 0);
+    SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 3);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<(H_STAGES - 3) * H_DMA + 5>();
+    wait_lgkm0();
+    bare_barrier();
+    // quarters 1-3: stage kt+1's sub-step-0 fragments into set 0 (3 + 3 + 2)
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int t = t0 + wt + j * 32 + lrow;
-    if (t >= T) continue;
-    uint16_t* krow = kv + (int64_t)t * N;
+    for (int q = 1; q < 4; ++q) {
+      __builtin_amdgcn_sched_barrier(0);
+      dma(pfb, kofs, 4 + q);
+      const int f0 = q == 1 ? 0 : (q == 2 ? 3 : 6), nf = q == 3 ? 2 : 3;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn + i * 32 + 8 * g + 4 * lhalf;
-        if (n + 4 <= N) {
-          uint2 o;
-          o.x = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
-          o.y = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-          *reinterpret_cast<uint2*>(krow + n) = o;
-        }
+      for (int f = 0; f < nf; ++f) frag(nxt, 0, 0, f0 + f);
+      mfma_row(1, q);
+      if (q < 3) {
+        SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1);
+        SGB(SG_DSR, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1);
+      } else {
+        SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1);
+        SGB(SG_MFMA, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1);
       }
+    }
+    cur = nxt;
   }
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vm<0>();   // the zero-fill DMAs of the last stages land before LDS is reused
+  store_tile(acc, smem, kv, T, N, t0, n0, wn, wt, lane, wave);
 }
 
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -231,7 +347,7 @@ void gemm_mxfp8_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  stage_load<false>(ra, rb, smem, wave, lane, row_bytes, 0, row_bytes);
+  stage_load(ra, rb, smem, wave, lane, row_bytes, 0);
   scale_load(0);
   __syncthreads();
 
@@ -241,8 +357,8 @@ void gemm_mxfp8_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict
 #pragma unroll
     for (int i = 0; i < 4; ++i) { csa[i] = sa[i]; csb[i] = sb[i]; }
     if (kt + 1 < nk) {
-      stage_load<false>(ra, rb, smem + ((kt + 1) & 1) * STAGE_BYTES, wave, lane, row_bytes,
-                        (uint32_t)(kt + 1) * 128u, row_bytes);
+      stage_load(ra, rb, smem + ((kt + 1) & 1) * STAGE_BYTES, wave, lane, row_bytes,
+                 (uint32_t)(kt + 1) * 128u);
       scale_load(kt + 1);
     }
     const uint4* As = reinterpret_cast<const uint4*>(cur);
@@ -273,24 +389,7 @@ void gemm_mxfp8_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict
     __syncthreads();
   }
 
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int t = t0 + wt + j * 32 + lrow;
-    if (t >= T) continue;
-    uint16_t* krow = kv + (int64_t)t * N;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int n = n0 + wn + i * 32 + 8 * g + 4 * lg;
-        if (n + 4 <= N) {
-          uint2 o;
-          o.x = pack_bf16x2(acc[i][j][4 * g + 0], acc[i][j][4 * g + 1]);
-          o.y = pack_bf16x2(acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]);
-          *reinterpret_cast<uint2*>(krow + n) = o;
-        }
-      }
-  }
+  store_tile(acc, smem, kv, T, N, t0, n0, wn, wt, lane, wave);
 }
 
 hipError_t set_lds(const void* fn) {
@@ -305,7 +404,7 @@ hipError_t launch_gemm_bf16(const void* x, int64_t T, int K, const void* w, int 
   const int tiles_t = (int)((T + BN - 1) / BN);
   const dim3 grid(tiles_n * tiles_t), block(THREADS);
   hipError_t e;
-  if (K % 64 == 0) {
+  if (K % 32 == 0) {
     if ((e = set_lds((const void*)gemm_bf16_kernel<false>)) != hipSuccess) return e;
     hipLaunchKernelGGL(gemm_bf16_kernel<false>, grid, block, LDS_BYTES, s, (const uint16_t*)x, (int)T, K,
                        (const uint16_t*)w, N, (uint16_t*)kv, tiles_n, tiles_t);

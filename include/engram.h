@@ -109,7 +109,9 @@ int engram_mx_quantize(const void* x, int64_t T, int32_t K, uint8_t* xq,
  *   workspace  device scratch of at least engram_wkv_workspace_size() bytes
  *              (NULL allowed when that size is 0). For MXFP8 it holds x's
  *              MXFP8 codes and scales. 256-byte aligned.
- *   Shapes: bf16 needs K % 8 == 0; MXFP8 needs K % 128 == 0 and N % 32 == 0.
+ *   Shapes: bf16 needs K % 8 == 0 and N % 4 == 0; MXFP8 needs K % 128 == 0
+ *   and N % 32 == 0; both need K <= 2^20 (32-bit buffer offsets). Other
+ *   shapes return ENGRAM_EUNSUPPORTED.
  */
 size_t engram_wkv_workspace_size(int64_t T, int32_t K, int32_t N,
                                  int32_t w_format);

@@ -238,7 +238,10 @@ def test_wkv(name):
 
 @pytest.mark.parametrize("fmt", ["bf16", "mxfp8"])
 @pytest.mark.parametrize("T,K,N", [(1, 256, 96), (17, 384, 288), (65, 512, 544), (300, 640, 800),
-                                   (513, 1024, 320), (64, 256, 768)])
+                                   (513, 1024, 320), (64, 256, 768),
+                                   # bf16 only: K % 32 != 0 (partial last k stage), N % 8 == 4
+                                   # (half 16-byte chunk at a row's end), K below one stage
+                                   (33, 264, 100), (257, 72, 260), (1, 8, 4)])
 def test_wkv_ragged_shapes(fmt, T, K, N):
     E = _E()
     g = torch.Generator(device=DEV).manual_seed(T * 7 + K + N)
@@ -249,8 +252,8 @@ def test_wkv_ragged_shapes(fmt, T, K, N):
         ref_bits, ref64 = o.wkv(bits(x), bits(w))
         _kv_checks(bits(kv), ref_bits, ref64, strict=True)
     else:
-        if K % 128:
-            pytest.skip("MXFP8 needs K % 128 == 0")
+        if K % 128 or N % 32:
+            pytest.skip("MXFP8 needs K % 128 == 0 and N % 32 == 0")
         w = torch.randn((N, K), generator=g, device=DEV).to(torch.float8_e4m3fn).view(torch.uint8)
         ws = (127 + torch.randint(-8, 1, (N // 32, K // 32), generator=g, device=DEV)).to(torch.uint8)
         kv = E.wkv(x, w, ws)
