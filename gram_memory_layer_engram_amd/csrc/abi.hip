@@ -1,6 +1,8 @@
 // C ABI of libengram: argument validation, workspace layout and dispatch.
 // Every entry point only enqueues work on the caller's stream.
 #include "../../include/engram.h"
+#include <algorithm>
+
 #include "common.h"
 
 #include <string.h>
@@ -172,7 +174,16 @@ int engram_gate(const void* hidden, const void* kv, const void* q_weight,
                                 dim, eps, clamp, out, gate_out, (hipStream_t)stream));
 }
 
-// Forward workspace: staged rows [T, K] bf16 | kv [T, N] bf16 | MXFP8 staging.
+// Forward workspace: a 64 KiB flag area (used by engram_forward_single_launch;
+// zero before the first call, left zero by every call), then staged rows
+// [T, K] bf16 | kv [T, N] bf16 | MXFP8 staging, or the single-launch
+// scratch, whichever is larger.
+constexpr size_t kSyncBytes = kDecodeSyncBytes;
+
+bool use_decode_path(const engram_forward_args* a, int32_t K, int32_t N) {
+  return a->w_format == ENGRAM_W_MXFP8 && decode_forward_supported(a->T, K, N, a->head_dim, a->dim, a->hc);
+}
+
 size_t engram_forward_workspace_size(const engram_forward_args* a) {
   if (!a || a->T <= 0 || a->n_cols <= 0 || a->head_dim <= 0 || a->hc <= 0 || a->dim <= 0)
     return 0;
@@ -180,33 +191,44 @@ size_t engram_forward_workspace_size(const engram_forward_args* a) {
   const int64_t N = (int64_t)(a->hc + 1) * a->dim;
   size_t bytes = round_up((size_t)a->T * K * 2) + round_up((size_t)a->T * N * 2);
   if (a->w_format == ENGRAM_W_MXFP8) bytes += mx_stage_bytes(a->T, (int32_t)K);
-  return bytes;
+  if (K <= INT32_MAX && N <= INT32_MAX && use_decode_path(a, (int32_t)K, (int32_t)N))
+    bytes = std::max(bytes, decode_forward_scratch_bytes(a->T, (int)K, (int)N, a->dim));
+  return kSyncBytes + bytes;
 }
 
-int engram_forward(const engram_forward_args* a, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+// Shared argument checks of the two forward entry points; sets K and N.
+int check_forward(const engram_forward_args* a, void* workspace, size_t workspace_bytes, int32_t* K,
+                  int32_t* N) {
   if (!a) return ENGRAM_EINVAL;
   const int64_t K64 = (int64_t)a->n_cols * a->head_dim;
   const int64_t N64 = (int64_t)(a->hc + 1) * a->dim;
   if (K64 > INT32_MAX || N64 > INT32_MAX) return ENGRAM_EUNSUPPORTED;
-  const int32_t K = (int32_t)K64, N = (int32_t)N64;
+  *K = (int32_t)K64;
+  *N = (int32_t)N64;
   int st = check_lookup(a->table, a->num_rows, a->head_dim, a->hash_ids, a->ids_stride_t,
                         a->ids_stride_c, a->T, a->n_cols, (void*)16);
   if (st != ENGRAM_OK) return st;
   st = check_gate(a->hidden, (void*)16, a->q_weight, a->k_weight, a->T, a->hc, a->dim, a->out);
   if (st != ENGRAM_OK) return st;
-  st = check_wkv((void*)16, a->T, K, a->w, a->w_scales, a->w_format, N, (void*)16);
+  st = check_wkv((void*)16, a->T, *K, a->w, a->w_scales, a->w_format, *N, (void*)16);
   if (st != ENGRAM_OK) return st;
   if (a->T == 0) return ENGRAM_OK;
   const size_t need = engram_forward_workspace_size(a);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign)) return ENGRAM_EINVAL;
+  return ENGRAM_OK;
+}
+
+int engram_forward(const engram_forward_args* a, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  int32_t K = 0, N = 0;
+  int st = check_forward(a, workspace, workspace_bytes, &K, &N);
+  if (st != ENGRAM_OK || a->T == 0) return st;
 
   hipStream_t s = (hipStream_t)stream;
-  uint8_t* ws = (uint8_t*)workspace;
+  uint8_t* ws = (uint8_t*)workspace + kSyncBytes;
   void* rows = ws;
   void* kv = ws + round_up((size_t)a->T * K * 2);
   void* mx = (uint8_t*)kv + round_up((size_t)a->T * N * 2);
-
   hipError_t e;
   if (a->w_format == ENGRAM_W_MXFP8 && a->head_dim % 32 == 0) {
     // the gather feeds the quantizer directly: bf16 staged rows never reach HBM
@@ -227,6 +249,20 @@ int engram_forward(const engram_forward_args* a, void* workspace,
   e = launch_gate(a->hidden, kv, a->q_weight, a->k_weight, a->token_mask, a->T, a->hc,
                   a->dim, a->eps, a->clamp, a->out, a->gate_out, s);
   return hip_status(e);
+}
+
+int engram_forward_single_launch(const engram_forward_args* a, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  int32_t K = 0, N = 0;
+  int st = check_forward(a, workspace, workspace_bytes, &K, &N);
+  if (st != ENGRAM_OK || a->T == 0) return st;
+  if (!use_decode_path(a, K, N)) return ENGRAM_EUNSUPPORTED;
+  uint8_t* ws = (uint8_t*)workspace + kSyncBytes;
+  return hip_status(launch_decode_forward(a->table, a->num_rows, a->head_dim, a->hash_ids, a->ids_stride_t,
+                                          a->ids_stride_c, a->n_cols, a->T, K, a->w, a->w_scales, N,
+                                          a->hidden, a->q_weight, a->k_weight, a->token_mask, a->hc,
+                                          a->dim, a->eps, a->clamp, a->out, a->gate_out, a->err_flag,
+                                          (uint32_t*)workspace, ws, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -72,5 +72,20 @@ constexpr int kGemvMaxT = 64;
 // its per-wave register budget.
 bool gemv_mxfp8_supported(int64_t T, int K);
 
+// Single-launch decode forward (MXFP8 wkv, T <= kGemvMaxT): shape support,
+// scratch it needs besides the counter area (kDecodeSyncBytes at the front of
+// the forward workspace: one counter and up to kDecodeMaxFlags per-workgroup
+// flags), and the launcher.
+constexpr size_t kDecodeSyncBytes = 64 * 1024;
+constexpr int kDecodeMaxFlags = (int)(kDecodeSyncBytes / 4) - 64;
+bool decode_forward_supported(int64_t T, int K, int N, int head_dim, int dim, int hc);
+size_t decode_forward_scratch_bytes(int64_t T, int K, int N, int dim);
+hipError_t launch_decode_forward(const void* table, int64_t num_rows, int head_dim, const int32_t* ids,
+                                 int64_t st, int64_t sc, int n_cols, int64_t T, int K, const void* w,
+                                 const uint8_t* w_scales, int N, const void* hidden, const void* q,
+                                 const void* k, const uint8_t* mask, int hc, int dim, float eps,
+                                 float clamp, void* out, float* gate_out, int32_t* err, uint32_t* sync,
+                                 uint8_t* scratch, hipStream_t s);
+
 
 }  // namespace engram

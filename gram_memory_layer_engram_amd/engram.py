@@ -50,6 +50,7 @@ EXPORTS = {
     "engram_gate": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _f32, _f32, _vp, _vp, _vp]),
     "engram_forward_workspace_size": (_sz, [ctypes.POINTER(ForwardArgs)]),
     "engram_forward": (_i32, [ctypes.POINTER(ForwardArgs), _vp, _sz, _vp]),
+    "engram_forward_single_launch": (_i32, [ctypes.POINTER(ForwardArgs), _vp, _sz, _vp]),
 }
 
 _lib = None
@@ -199,8 +200,10 @@ def forward_workspace_size(args: ForwardArgs) -> int:
 
 
 def forward(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask=None,
-            eps=1e-6, clamp=1e-6, out=None, gate_out=None, err_flag=None, workspace=None):
-    """One Engram layer forward: lookup -> (MXFP8 quantize) -> wkv -> gate."""
+            eps=1e-6, clamp=1e-6, out=None, gate_out=None, err_flag=None, workspace=None,
+            single_launch=False):
+    """One Engram layer forward: lookup -> (MXFP8 quantize) -> wkv -> gate.
+    ``single_launch`` selects engram_forward_single_launch (decode shapes)."""
     L = load_library()
     for t, n in ((table, "table"), (w, "w"), (hidden, "hidden"),
                  (q_weight, "q_weight"), (k_weight, "k_weight")):
@@ -211,10 +214,17 @@ def forward(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask
                         eps, clamp, out, gate_out, err_flag)
     need = L.engram_forward_workspace_size(ctypes.byref(args))
     if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=hidden.device)
+        workspace = new_forward_workspace(need, hidden.device)
     ws_bytes = 0 if workspace is None else workspace.numel()
-    _check(L.engram_forward(ctypes.byref(args), _ptr(workspace), ws_bytes, _stream()))
+    fn = L.engram_forward_single_launch if single_launch else L.engram_forward
+    _check(fn(ctypes.byref(args), _ptr(workspace), ws_bytes, _stream()))
     return out
+
+
+def new_forward_workspace(nbytes: int, device) -> torch.Tensor:
+    """A forward workspace: its leading 64 KiB of flags start at zero (every
+    call leaves them zero again), so it is allocated zeroed once."""
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
 
 
 class ForwardPlan:
@@ -225,7 +235,7 @@ class ForwardPlan:
 
     def __init__(self, table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask=None,
                  eps=1e-6, clamp=1e-6, out=None, gate_out=None, err_flag=None, workspace=None,
-                 stream=None):
+                 stream=None, single_launch=False):
         L = load_library()
         for t, n in ((table, "table"), (w, "w"), (hidden, "hidden"),
                      (q_weight, "q_weight"), (k_weight, "k_weight")):
@@ -239,12 +249,12 @@ class ForwardPlan:
                                  eps, clamp, out, gate_out, err_flag)
         need = L.engram_forward_workspace_size(ctypes.byref(self.args))
         if workspace is None and need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=hidden.device)
+            workspace = new_forward_workspace(need, hidden.device)
         self.workspace = workspace
         self._ws = _ptr(workspace)
         self._ws_bytes = 0 if workspace is None else workspace.numel()
         self._argp = ctypes.byref(self.args)
-        self._fn = L.engram_forward
+        self._fn = L.engram_forward_single_launch if single_launch else L.engram_forward
         self._stream = (torch.cuda.current_stream() if stream is None else stream).cuda_stream
 
     def run(self):

@@ -154,6 +154,12 @@ int engram_gate(const void* hidden, const void* kv, const void* q_weight,
  *   EngramPrefetch's per-layer kv buffers).
  *   Field meanings are those of the calls above; K = n_cols*head_dim and
  *   N = (hc+1)*dim.
+ *   workspace  engram_forward_workspace_size() bytes, 256-byte aligned; its
+ *              first 64 KiB are the flag area of
+ *              engram_forward_single_launch (zero before the first call of
+ *              that entry point on the workspace; left zero by every call).
+ *   err_flag   bit 0: an id outside [0, num_rows) (zero row used); bit 1:
+ *              see engram_forward_single_launch. Never cleared by the call.
  */
 typedef struct engram_forward_args {
   const void* table;       /* bf16 [num_rows, head_dim] */
@@ -177,12 +183,38 @@ typedef struct engram_forward_args {
   float clamp;
   void* out;               /* bf16 [T, hc, dim] */
   float* gate_out;         /* optional fp32 [T, hc] */
-  int32_t* err_flag;       /* optional, see engram_lookup */
+  int32_t* err_flag;       /* optional int32 device flag, bits above */
 } engram_forward_args;
 
 size_t engram_forward_workspace_size(const engram_forward_args* a);
 int engram_forward(const engram_forward_args* a, void* workspace,
                    size_t workspace_bytes, void* stream);
+
+/*
+ * engram_forward_single_launch -- the same forward for decode batches as ONE
+ *   kernel: gather, MXFP8 quantize, weight-streaming GEMV and the gate, the
+ *   gate's kv-side sums taken as per-tile partials and finished in-launch,
+ *   the split of [P-rocm] _engram_gate_partials_kernel /
+ *   _engram_gate_finish_kernel (one shard). Same arguments, workspace size
+ *   and results (to rounding of the gate's sums) as engram_forward.
+ *   Supported: w_format ENGRAM_W_MXFP8, 1 <= T <= 64, K % 1024 == 0,
+ *   head_dim % 32 == 0, dim % 16 == 0, T*K <= 128 KiB; else
+ *   ENGRAM_EUNSUPPORTED.
+ *   Its workgroups coordinate through flags in the first 64 KiB of the
+ *   workspace:
+ *     - those bytes must be zero before the first call on a workspace
+ *       (allocate it zeroed); every call returns them to zero;
+ *     - calls sharing a workspace must be ordered on one stream;
+ *     - flags found raised on entry, or a wait that timed out (the launch
+ *       starved of compute units for 200 ms), set bit 1 (value 2) of
+ *       *err_flag and the outputs are not valid; zero those 64 KiB again
+ *       before the next call.
+ *   On MI355X it is slower than engram_forward at the decode sizes measured
+ *   (the hand-offs between workgroups cost more than the launch gaps they
+ *   remove), so engram_forward does not use it.
+ */
+int engram_forward_single_launch(const engram_forward_args* a, void* workspace,
+                                 size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

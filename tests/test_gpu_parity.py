@@ -429,9 +429,10 @@ def test_forward_small_hidden_engram_term_dominates():
 
 @pytest.mark.parametrize("T", [1, 5, 16, 17, 31, 32, 33, 64, 65])
 def test_forward_mxfp8_decode_paths_and_bad_ids(T):
-    """T <= 64 runs the fused gather+quantize launch and the decode GEMV, 65
-    the scaled-MFMA GEMM; all against the oracle, with one out-of-range id
-    (zero row + flag)."""
+    """K = 512 (not a multiple of 1024): T <= 64 runs the fused
+    gather+quantize launch, the decode GEMV and the gate kernel, 65 the
+    scaled-MFMA GEMM; all against the oracle, with one out-of-range id (zero
+    row + flag)."""
     E = _E()
     g = torch.Generator(device=DEV).manual_seed(1000 + T)
     R, C, hd, dim, hc = 3001, 4, 128, 256, 2
@@ -458,6 +459,92 @@ def test_forward_mxfp8_decode_paths_and_bad_ids(T):
     assert ref["err"]
     assert_close(bf16_values(bits(out)), bf16_values(ref["out"]), *OUT_TOL, what="out")
     assert np.max(np.abs(gate_out.cpu().numpy() - ref["gate"])) <= 2e-2
+
+
+def _decode_case(T, dim, hc, seed, C=8, hd=128, R=4001):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    K, N = C * hd, (hc + 1) * dim
+    table = (torch.randn((R, hd), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    ids = torch.randint(0, R, (T, C), generator=g, device=DEV, dtype=torch.int32)
+    w = torch.randn((N, K), generator=g, device=DEV).to(torch.float8_e4m3fn).view(torch.uint8)
+    ws = (127 + torch.randint(-8, 1, (N // 32, K // 32), generator=g, device=DEV)).to(torch.uint8)
+    hidden = torch.randn((T, hc, dim), generator=g, device=DEV).to(torch.bfloat16)
+    q = (1 + 0.1 * torch.randn((hc, dim), generator=g, device=DEV)).to(torch.bfloat16)
+    k = (1 + 0.1 * torch.randn((hc, dim), generator=g, device=DEV)).to(torch.bfloat16)
+    mask = torch.rand((T,), generator=g, device=DEV) > 0.2
+    return dict(table=table, ids=ids, w=w, ws=ws, hidden=hidden, q=q, k=k, mask=mask)
+
+
+def _decode_ref(c):
+    return o.forward(bits(c["table"]), c["ids"].cpu().numpy(), u8(c["w"]), u8(c["ws"]), bits(c["hidden"]),
+                     bits(c["q"]), bits(c["k"]), c["mask"].cpu().numpy(), 1e-6, 1e-6)
+
+
+@pytest.mark.parametrize("T,dim,hc", [(1, 256, 2), (5, 256, 2), (16, 256, 2), (17, 256, 2), (33, 256, 2),
+                                      (64, 256, 2), (16, 1024, 4), (3, 1024, 4)])
+def test_forward_single_launch_decode(T, dim, hc):
+    """engram_forward_single_launch (K % 1024 == 0, T <= 64): gather,
+    quantize, GEMV and gate run as one launch whose workgroups hand the gate
+    partials over through the workspace. Checked against the oracle with a
+    masked share of tokens and one out-of-range id; repeated calls on one
+    plan are bit-identical and leave the workspace flags at zero."""
+    E = _E()
+    c = _decode_case(T, dim, hc, seed=7000 + T + dim)
+    c["ids"][T // 2, 3] = -5
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    gate_out = torch.empty((T, hc), dtype=torch.float32, device=DEV)
+    plan = E.ForwardPlan(c["table"], c["ids"], c["w"], c["ws"], c["hidden"], c["q"], c["k"], c["mask"],
+                         gate_out=gate_out, err_flag=err, single_launch=True)
+    out = plan.run().clone()
+    out2 = plan.run()
+    torch.cuda.synchronize()
+    assert int(err.item()) == 1
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert int(plan.workspace[:65536].count_nonzero().item()) == 0
+    ref = _decode_ref(c)
+    assert ref["err"]
+    assert_close(bf16_values(bits(out)), bf16_values(ref["out"]), *OUT_TOL, what="out")
+    m = c["mask"].cpu().numpy()
+    assert np.array_equal(bits(out)[~m], bits(c["hidden"])[~m])
+    assert np.max(np.abs(gate_out.cpu().numpy() - ref["gate"])) <= 2e-2
+
+
+def test_forward_single_launch_unsupported_shapes_are_refused():
+    """Shapes outside the single launch (bf16 wkv, T > 64, K % 1024 != 0)
+    are refused with ValueError, nothing launched; engram_forward serves
+    them."""
+    E = _E()
+    c = _decode_case(65, 256, 2, seed=5)
+    with pytest.raises(ValueError):
+        E.forward(c["table"], c["ids"], c["w"], c["ws"], c["hidden"], c["q"], c["k"], c["mask"],
+                  single_launch=True)
+    c = _decode_case(8, 256, 2, seed=6, C=4)          # K = 512
+    with pytest.raises(ValueError):
+        E.forward(c["table"], c["ids"], c["w"], c["ws"], c["hidden"], c["q"], c["k"], c["mask"],
+                  single_launch=True)
+
+
+def test_forward_single_launch_decode_flags_dirty_counters():
+    """Flags left raised (here forced from the host) are detected: bit 1 of
+    the error flag is raised and the kernel still exits; after zeroing them
+    the next call is correct again."""
+    E = _E()
+    T, dim, hc = 4, 256, 2
+    c = _decode_case(T, dim, hc, seed=99)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    plan = E.ForwardPlan(c["table"], c["ids"], c["w"], c["ws"], c["hidden"], c["q"], c["k"], c["mask"],
+                         err_flag=err, single_launch=True)
+    plan.workspace[:65536].view(torch.int32).fill_(1)
+    plan.run()
+    torch.cuda.synchronize()
+    assert int(err.item()) & 2
+    plan.workspace[:65536].zero_()
+    err.zero_()
+    out = plan.run()
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    ref = _decode_ref(c)
+    assert_close(bf16_values(bits(out)), bf16_values(ref["out"]), *OUT_TOL, what="out")
 
 
 def test_forward_plan_graph_replay():
