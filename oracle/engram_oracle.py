@@ -9,7 +9,8 @@ follows, which are the vLLM API pages:
 
 * "vllm.models.deepseek_v4_1.common.engram" -- class ``Engram`` (docstring,
   ``__init__``, ``prepare_embeddings``, ``forward``), class ``EngramLayout``,
-  class ``ParallelEngramEmbedding`` (``lookup``, ``forward``);
+  class ``ParallelEngramEmbedding`` (docstring, ``__init__``, ``lookup``,
+  ``forward``);
 * "vllm.models.deepseek_v41.amd.engram" -- ``_engram_gate_finish_kernel`` and
   ``_engram_gate_partials_kernel`` (the gate math, the only place the pages
   print it in full);
@@ -31,6 +32,9 @@ Parity status per function (each is pinned by ``tests/test_oracle_pins.py``):
 * ``mx_quantize``          -- pinned to the OCP MX v1.0 rule by worked blocks
                               and invariants; the pages do not fix the rule
 * ``gather_rows``          -- pinned (direct indexing)
+* ``dequant_table_rows``   -- pinned (library fp8 cast, worked extremes in
+                              ``tests/golden/fp8_table_dequant.json``)
+* ``gather_rows_fp8``      -- pinned (gather and dequant commute; zero rows)
 * ``wkv``                  -- pinned (brute-force loops, one-hot scale probes)
 * ``gate`` / ``gate_partials`` / ``gate_finish`` -- pinned (closed forms,
                               second route, invariants)
@@ -235,6 +239,47 @@ def gather_rows(table_bits, hash_ids):
     return rows, bool(bad.any())
 
 
+def dequant_table_rows(codes, scale_bytes):
+    """fp8 table rows ``[..., hd]`` e4m3fn + ``[..., hd/32]`` ue8m0 bytes ->
+    bf16 bit patterns ``[..., hd]``.
+
+    "vllm.models.deepseek_v4_1.common.engram", ``ParallelEngramEmbedding``
+    (class docstring and ``__init__``): the table is ``[rows, dim]``
+    float8_e4m3fn plus one uint8 ue8m0 scale per row and 32 consecutive
+    elements (``weight_scale_inv``, ``[rows, dim // block_size]``,
+    block_size 32), and rows are dequantized to bf16 on lookup. The pages do
+    not print the arithmetic; the reading taken is the plain one: element
+    value times 2**(byte - 127) (E8M0: byte 255 is NaN), rounded to bf16
+    (nearest even; beyond the bf16 range -> inf, below half its smallest
+    subnormal -> 0). In the ordinary range the product is exact in bf16
+    (e4m3 keeps 3 fraction bits, bf16 7), so the rounding only acts at the
+    extremes.
+    """
+    c = np.asarray(codes, dtype=np.uint8)
+    s = np.asarray(scale_bytes, dtype=np.uint8)
+    if c.shape[-1] != s.shape[-1] * MX_BLOCK:
+        raise ValueError("one scale byte per 32 elements")
+    scale = np.repeat(e8m0_decode(s), MX_BLOCK, axis=-1)
+    return round_to_bf16(e4m3fn_decode(c) * scale)
+
+
+def gather_rows_fp8(table_codes, table_scales, hash_ids):
+    """``rows[t, c, :] = dequant(table[hash_ids[t, c], :])`` as bf16 bits,
+    the lookup of an fp8 table ("vllm.models.deepseek_v4_1.common.engram",
+    ``ParallelEngramEmbedding``: rows stay fp8 and are dequantized with their
+    per-32 scales on lookup). Out-of-range ids: zero row + error flag, as in
+    ``gather_rows``."""
+    codes = np.asarray(table_codes, dtype=np.uint8)
+    scales = np.asarray(table_scales, dtype=np.uint8)
+    ids = np.asarray(hash_ids, dtype=np.int64)
+    num_rows = codes.shape[0]
+    bad = (ids < 0) | (ids >= num_rows)
+    safe = np.where(bad, 0, ids)
+    rows = dequant_table_rows(codes[safe], scales[safe])
+    rows[bad] = 0
+    return rows, bool(bad.any())
+
+
 # ---------------------------------------------------------------------------
 # Step 2: wkv projection
 # ---------------------------------------------------------------------------
@@ -372,13 +417,15 @@ def gate_finish(hidden_bits, parts, token_mask, eps, clamp):
 
 
 def forward(table_bits, hash_ids, w, w_scales, hidden_bits, q_bits, k_bits,
-            token_mask, eps, clamp, block_tokens=2048):
+            token_mask, eps, clamp, block_tokens=2048, table_scales=None):
     """One Engram layer forward: gather -> (MXFP8 quantize) -> wkv -> gate.
 
     "vllm.models.deepseek_v4_1.common.engram", ``Engram.forward``:
     ``kv = wkv(embed(hash_ids).flatten(-2))``, then the fused gate / residual
     over ``[T, hc, dim]``. Every output row depends only on its own token's
     ids, hidden row and mask bit, so the work is done in token blocks (exact).
+    With ``table_scales`` the table is fp8 (``table_bits`` holds e4m3fn codes)
+    and the gather dequantizes (``gather_rows_fp8``).
     Returns dict(rows, kv, gate, out, err).
     """
     hidden_bits = np.asarray(hidden_bits, dtype=np.uint16)
@@ -397,7 +444,10 @@ def forward(table_bits, hash_ids, w, w_scales, hidden_bits, q_bits, k_bits,
         wa = mx_dequantize_weight(w, w_scales)
     for t0 in range(0, T, block_tokens):
         t1 = min(T, t0 + block_tokens)
-        r, e = gather_rows(table_bits, ids[t0:t1])
+        if table_scales is None:
+            r, e = gather_rows(table_bits, ids[t0:t1])
+        else:
+            r, e = gather_rows_fp8(table_bits, table_scales, ids[t0:t1])
         err |= e
         rows[t0:t1] = r
         x = r.reshape(t1 - t0, C * hd)

@@ -189,6 +189,71 @@ def test_gather_equals_direct_indexing_and_flags_bad_ids():
     assert np.array_equal(rows[2, 0], table[ids[2, 0]])
 
 
+# ------------------------------------------------------------ fp8 tables ----
+
+
+def test_fp8_table_dequant_worked_values():
+    """Hand-worked e4m3 x 2^(b-127) -> bf16 cases, incl. the range edges
+    (tests/golden/fp8_table_dequant.json states the source and each step)."""
+    cases = json.load(open(os.path.join(GOLDEN, "fp8_table_dequant.json")))["cases"]
+    for c in cases:
+        codes = np.full((1, 32), int(c["code"], 16), np.uint8)
+        sb = np.array([[c["byte"]]], np.uint8)
+        got = o.dequant_table_rows(codes, sb)
+        assert np.all(got == int(c["bf16"], 16)), (c, hex(int(got[0, 0])))
+
+
+def test_fp8_table_dequant_matches_library_fp8_cast():
+    """Every e4m3 code under scale bytes 100..167, a different byte for each
+    32-element block of a row (so a wrong block-to-scale mapping shows):
+    torch's float8_e4m3fn decode, times the power of two in float32 (exact
+    there), cast to bfloat16 by torch."""
+    codes = np.tile(np.arange(256, dtype=np.uint8), (61, 1))           # [61, 256]: 8 blocks a row
+    sb = (np.arange(100, 161)[:, None] + np.arange(8)[None, :]).astype(np.uint8)   # [61, 8]
+    got = o.dequant_table_rows(codes, sb)
+    per_elem = np.repeat(sb.astype(np.int64), 32, axis=1)              # element j uses block j // 32
+    f = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float32)
+    f = f * torch.from_numpy(np.ldexp(1.0, per_elem - 127).astype(np.float32))
+    want = f.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    nan = np.isnan(f.numpy())
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.all(got[nan] == 0x7FC0)
+
+
+def test_gather_rows_fp8_commutes_with_dequant_and_flags_bad_ids():
+    rng = np.random.default_rng(15)
+    codes = rng.integers(0, 256, size=(61, 64), dtype=np.uint8)
+    codes[(codes & 0x7F) == 0x7F] = 0x11                                # no NaN codes
+    scales = rng.integers(110, 135, size=(61, 2), dtype=np.uint8)
+    ids = rng.integers(0, 61, size=(9, 3))
+    ids[4, 2] = 61
+    ids[7, 0] = -3
+    rows, err = o.gather_rows_fp8(codes, scales, ids)
+    assert err
+    full = o.dequant_table_rows(codes, scales)
+    for t in range(9):
+        for c in range(3):
+            if 0 <= ids[t, c] < 61:
+                assert np.array_equal(rows[t, c], full[ids[t, c]])
+            else:
+                assert not rows[t, c].any()
+
+
+def test_forward_fp8_table_equals_forward_on_dequantized_table():
+    rng = np.random.default_rng(16)
+    T, hc, dim, C, hd, R = 19, 2, 64, 4, 32, 173
+    codes = torch.from_numpy(rng.standard_normal((R, hd))).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    scales = rng.integers(119, 124, size=(R, hd // 32)).astype(np.uint8)
+    ids = rng.integers(0, R, size=(T, C))
+    w = o.round_to_bf16(rng.standard_normal(((hc + 1) * dim, C * hd)) * 0.02)
+    hidden, _, q, k = _rand_gate_inputs(rng, T, hc, dim)
+    mask = rng.random(T) > 0.2
+    a = o.forward(codes, ids, w, None, hidden, q, k, mask, EPS, CLAMP, table_scales=scales)
+    b = o.forward(o.dequant_table_rows(codes, scales), ids, w, None, hidden, q, k, mask, EPS, CLAMP)
+    for key in ("rows", "kv", "out", "gate"):
+        assert np.array_equal(a[key], b[key]), key
+
+
 # ------------------------------------------------------------------ wkv ----
 
 
