@@ -99,11 +99,25 @@ def bench_prefill(steps, warmup):
     rows = torch.empty((wl.T, wl.C, wl.head_dim), dtype=torch.bfloat16, device="cuda")
     kv = torch.empty((wl.T, wl.N), dtype=torch.bfloat16, device="cuda")
     x = rows.view(wl.T, wl.K)
-    t_lookup = _events_time(lambda i: E.lookup(inp["table"], inp["ids"], rows_out=rows), steps, stream)
+    L = E.load_library()
+    sp = stream.cuda_stream
+    ids = inp["ids"]
+    look = (inp["table"].data_ptr(), inp["table"].shape[0], wl.head_dim, ids.data_ptr(), ids.stride(0),
+            ids.stride(1), wl.T, wl.C, rows.data_ptr(), None, sp)
+    t_lookup = _events_time(lambda i: L.engram_lookup(*look), steps, stream)
     t_wkv = _events_time(lambda i: E.wkv(x, inp["w"], kv=kv), steps, stream)
     t_gate = _events_time(lambda i: E.gate(inp["hidden"], kv, inp["q"], inp["k"], None, wl.eps,
                                            wl.clamp, out=out), steps, stream)
-    return wl, dt, {"lookup": t_lookup, "wkv": t_wkv, "gate": t_gate}
+    # the same gather from the table stored as fp8 (e4m3 + ue8m0 per 32), dequantized on lookup
+    del inp["table"]
+    torch.cuda.empty_cache()
+    codes, scales = W.make_table_fp8(wl, "cuda")
+    look8 = (codes.data_ptr(), scales.data_ptr(), codes.shape[0], wl.head_dim, ids.data_ptr(), ids.stride(0),
+             ids.stride(1), wl.T, wl.C, rows.data_ptr(), None, sp)
+    for _ in range(warmup):
+        L.engram_lookup_fp8(*look8)
+    t_lookup8 = _events_time(lambda i: L.engram_lookup_fp8(*look8), steps, stream)
+    return wl, dt, {"lookup": t_lookup, "wkv": t_wkv, "gate": t_gate, "lookup_fp8": t_lookup8}
 
 
 def bench_decode(steps, warmup, copies=16):
@@ -254,10 +268,13 @@ def main():
     }
     # the HBM-bound kernels of the same step, against 8 TB/s
     lookup_bytes = wl.T * wl.C * (4 + 2 * 2 * wl.head_dim)
+    lookup8_bytes = wl.T * wl.C * (4 + wl.head_dim + wl.head_dim // 32 + 2 * wl.head_dim)
     gate_bytes = wl.T * (2 * wl.hc * wl.dim + (wl.hc + 1) * wl.dim) * 2
     kernels = {
         "lookup_us": round(avg["lookup"] * 1e3, 2),
         "lookup_GBs": round(lookup_bytes / (avg["lookup"] * 1e-3) / 1e9, 1),
+        "lookup_fp8_table_us": round(avg["lookup_fp8"] * 1e3, 2),
+        "lookup_fp8_table_GBs": round(lookup8_bytes / (avg["lookup_fp8"] * 1e-3) / 1e9, 1),
         "wkv_us": round(avg["wkv"] * 1e3, 2), "wkv_us_median": round(med["wkv"] * 1e3, 2),
         "gate_us": round(avg["gate"] * 1e3, 2),
         "gate_GBs": round(gate_bytes / (avg["gate"] * 1e-3) / 1e9, 1),

@@ -109,6 +109,15 @@ int check_lookup(const void* table, int64_t num_rows, int32_t head_dim,
   return ENGRAM_OK;
 }
 
+int check_lookup_fp8(const void* codes, const uint8_t* scales, int64_t num_rows, int32_t head_dim,
+                     const int32_t* ids, int64_t st, int64_t sc, int64_t T, int32_t n_cols, void* rows_out) {
+  int st_ = check_lookup(codes, num_rows, head_dim, ids, st, sc, T, n_cols, rows_out);
+  if (st_ != ENGRAM_OK) return st_;
+  if (head_dim % 32 != 0) return ENGRAM_EUNSUPPORTED;
+  if (T > 0 && !scales) return ENGRAM_EINVAL;
+  return ENGRAM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -135,6 +144,18 @@ int engram_lookup(const void* table, int64_t num_rows, int32_t head_dim,
   return hip_status(launch_lookup(table, num_rows, head_dim, hash_ids, ids_stride_t,
                                   ids_stride_c, T, n_cols, rows_out, err_flag,
                                   (hipStream_t)stream));
+}
+
+int engram_lookup_fp8(const void* table_codes, const uint8_t* table_scales, int64_t num_rows,
+                      int32_t head_dim, const int32_t* hash_ids, int64_t ids_stride_t,
+                      int64_t ids_stride_c, int64_t T, int32_t n_cols, void* rows_out,
+                      int32_t* err_flag, void* stream) {
+  int st = check_lookup_fp8(table_codes, table_scales, num_rows, head_dim, hash_ids, ids_stride_t,
+                            ids_stride_c, T, n_cols, rows_out);
+  if (st != ENGRAM_OK || T == 0) return st;
+  return hip_status(launch_lookup_fp8(table_codes, table_scales, num_rows, head_dim, hash_ids,
+                                      ids_stride_t, ids_stride_c, T, n_cols, rows_out, err_flag,
+                                      (hipStream_t)stream));
 }
 
 int engram_mx_quantize(const void* x, int64_t T, int32_t K, uint8_t* xq,
@@ -205,8 +226,11 @@ int check_forward(const engram_forward_args* a, void* workspace, size_t workspac
   if (K64 > INT32_MAX || N64 > INT32_MAX) return ENGRAM_EUNSUPPORTED;
   *K = (int32_t)K64;
   *N = (int32_t)N64;
-  int st = check_lookup(a->table, a->num_rows, a->head_dim, a->hash_ids, a->ids_stride_t,
-                        a->ids_stride_c, a->T, a->n_cols, (void*)16);
+  int st = a->table_scales
+               ? check_lookup_fp8(a->table, a->table_scales, a->num_rows, a->head_dim, a->hash_ids,
+                                  a->ids_stride_t, a->ids_stride_c, a->T, a->n_cols, (void*)16)
+               : check_lookup(a->table, a->num_rows, a->head_dim, a->hash_ids, a->ids_stride_t,
+                              a->ids_stride_c, a->T, a->n_cols, (void*)16);
   if (st != ENGRAM_OK) return st;
   st = check_gate(a->hidden, (void*)16, a->q_weight, a->k_weight, a->T, a->hc, a->dim, a->out);
   if (st != ENGRAM_OK) return st;
@@ -234,14 +258,17 @@ int engram_forward(const engram_forward_args* a, void* workspace,
     // the gather feeds the quantizer directly: bf16 staged rows never reach HBM
     uint8_t* xq = (uint8_t*)mx;
     uint8_t* xs = xq + round_up((size_t)a->T * K);
-    e = launch_gather_quantize(a->table, a->num_rows, a->head_dim, a->hash_ids, a->ids_stride_t,
-                               a->ids_stride_c, a->T, a->n_cols, xq, xs, a->err_flag, s);
+    e = launch_gather_quantize(a->table, a->table_scales, a->num_rows, a->head_dim, a->hash_ids,
+                               a->ids_stride_t, a->ids_stride_c, a->T, a->n_cols, xq, xs, a->err_flag, s);
     if (e != hipSuccess) return ENGRAM_EHIP;
     e = run_mx_projection(xq, xs, a->T, K, a->w, a->w_scales, N, kv, s);
     if (e != hipSuccess) return ENGRAM_EHIP;
   } else {
-    e = launch_lookup(a->table, a->num_rows, a->head_dim, a->hash_ids, a->ids_stride_t,
-                      a->ids_stride_c, a->T, a->n_cols, rows, a->err_flag, s);
+    e = a->table_scales
+            ? launch_lookup_fp8(a->table, a->table_scales, a->num_rows, a->head_dim, a->hash_ids,
+                                a->ids_stride_t, a->ids_stride_c, a->T, a->n_cols, rows, a->err_flag, s)
+            : launch_lookup(a->table, a->num_rows, a->head_dim, a->hash_ids, a->ids_stride_t,
+                            a->ids_stride_c, a->T, a->n_cols, rows, a->err_flag, s);
     if (e != hipSuccess) return ENGRAM_EHIP;
     st = run_wkv(rows, a->T, K, a->w, a->w_scales, a->w_format, N, kv, mx, s);
     if (st != ENGRAM_OK) return st;
@@ -256,7 +283,7 @@ int engram_forward_single_launch(const engram_forward_args* a, void* workspace,
   int32_t K = 0, N = 0;
   int st = check_forward(a, workspace, workspace_bytes, &K, &N);
   if (st != ENGRAM_OK || a->T == 0) return st;
-  if (!use_decode_path(a, K, N)) return ENGRAM_EUNSUPPORTED;
+  if (a->table_scales || !use_decode_path(a, K, N)) return ENGRAM_EUNSUPPORTED;
   uint8_t* ws = (uint8_t*)workspace + kSyncBytes;
   return hip_status(launch_decode_forward(a->table, a->num_rows, a->head_dim, a->hash_ids, a->ids_stride_t,
                                           a->ids_stride_c, a->n_cols, a->T, K, a->w, a->w_scales, N,

@@ -48,11 +48,17 @@ hipError_t launch_gate(const void* hidden, const void* kv, const void* q,
 hipError_t launch_mx_quantize(const void* x, int64_t T, int K, uint8_t* xq,
                               uint8_t* xs, hipStream_t s);
 
-// Row gather fused with the MXFP8 quantizer (head_dim % 32 == 0).
-hipError_t launch_gather_quantize(const void* table, int64_t num_rows, int head_dim,
-                                  const int32_t* ids, int64_t st, int64_t sc, int64_t T,
-                                  int n_cols, uint8_t* xq, uint8_t* xs, int32_t* err,
-                                  hipStream_t s);
+// Row gather fused with the MXFP8 quantizer (head_dim % 32 == 0); an fp8
+// table when table_scales is not null.
+hipError_t launch_gather_quantize(const void* table, const uint8_t* table_scales, int64_t num_rows,
+                                  int head_dim, const int32_t* ids, int64_t st, int64_t sc, int64_t T,
+                                  int n_cols, uint8_t* xq, uint8_t* xs, int32_t* err, hipStream_t s);
+
+// Row gather from an fp8 table (e4m3 codes [rows, head_dim], ue8m0 bytes
+// [rows, head_dim / 32]) into bf16 rows; head_dim % 32 == 0.
+hipError_t launch_lookup_fp8(const void* codes, const uint8_t* scales, int64_t num_rows, int head_dim,
+                             const int32_t* ids, int64_t st, int64_t sc, int64_t T, int n_cols, void* out,
+                             int32_t* err, hipStream_t s);
 
 hipError_t launch_gemm_bf16(const void* x, int64_t T, int K, const void* w,
                             int N, void* kv, hipStream_t s);

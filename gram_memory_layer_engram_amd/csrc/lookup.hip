@@ -6,7 +6,12 @@
 // TLB reach. Here each thread moves 16-byte pieces of rows (head_dim*2/16
 // pieces per row), keeps UNROLL independent pieces in flight (id load, then
 // row load, then store), and strides over the whole [T*C*pieces] range.
+//
+// fp8 tables (same page, ParallelEngramEmbedding: rows stay fp8 and are
+// dequantized with their ue8m0 per-32 scales on lookup): a thread takes a
+// 32-element block, 32 code bytes + 1 scale byte in, 64 bf16 bytes out.
 #include "common.h"
+#include "fp8_table.h"
 
 namespace engram {
 
@@ -69,7 +74,72 @@ hipError_t launch_cpr(const void* table, int64_t num_rows, const int32_t* ids,
   return hipGetLastError();
 }
 
+// fp8 rows: grid-stride over 32-element blocks (total = T*C*bpr), two
+// blocks in flight per thread.
+__global__ __launch_bounds__(kLookupThreads) void lookup_fp8_kernel(
+    const uint4* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t num_rows, int bpr,
+    const int32_t* __restrict__ ids, int64_t st, int64_t sc, int n_cols, int64_t total,
+    uint4* __restrict__ out, int32_t* __restrict__ err) {
+  constexpr int U = 2;
+  const int64_t stride = (int64_t)gridDim.x * kLookupThreads;
+  int bad = 0;
+  for (int64_t base = (int64_t)blockIdx.x * kLookupThreads + threadIdx.x; base < total; base += stride * U) {
+    int64_t src[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + u * stride;
+      src[u] = -1;
+      if (i < total) {
+        const int64_t row = i / bpr;
+        const int part = (int)(i - row * bpr);
+        const int64_t t = row / n_cols;
+        const int c = (int)(row - t * n_cols);
+        const int64_t id = ids[t * st + (int64_t)c * sc];
+        if (id >= 0 && id < num_rows) src[u] = id * bpr + part;   // block index in the table
+        else bad = 1;
+      }
+    }
+    uint4 cv[U][2];
+    uint32_t sb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      cv[u][0] = cv[u][1] = make_uint4(0, 0, 0, 0);
+      sb[u] = 127u;
+      if (src[u] >= 0) {
+        cv[u][0] = codes[src[u] * 2];
+        cv[u][1] = codes[src[u] * 2 + 1];
+        sb[u] = scales[src[u]];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + u * stride;
+      if (i >= total) continue;
+      const uint32_t cw[8] = {cv[u][0].x, cv[u][0].y, cv[u][0].z, cv[u][0].w,
+                              cv[u][1].x, cv[u][1].y, cv[u][1].z, cv[u][1].w};
+      uint32_t o[16];
+      fp8_block_to_bf16(cw, sb[u], o);      // a bad id: zero codes, scale 1 -> zero row
+#pragma unroll
+      for (int q = 0; q < 4; ++q) out[i * 4 + q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+    }
+  }
+  if (bad && err) atomicOr(err, 1);
+}
+
 }  // namespace
+
+hipError_t launch_lookup_fp8(const void* codes, const uint8_t* scales, int64_t num_rows, int head_dim,
+                             const int32_t* ids, int64_t st, int64_t sc, int64_t T, int n_cols, void* out,
+                             int32_t* err, hipStream_t s) {
+  const int bpr = head_dim / 32;
+  const int64_t total = T * n_cols * bpr;
+  const int64_t need = (total + kLookupThreads * 2 - 1) / (kLookupThreads * 2);
+  const int64_t cap = (int64_t)dev_info().num_cus * 8;
+  const int grid = (int)(need < cap ? need : cap);
+  hipLaunchKernelGGL(lookup_fp8_kernel, dim3(grid), dim3(kLookupThreads), 0, s, (const uint4*)codes, scales,
+                     num_rows, bpr, ids, st, sc, n_cols, total, (uint4*)out, err);
+  return hipGetLastError();
+}
 
 hipError_t launch_lookup(const void* table, int64_t num_rows, int head_dim,
                          const int32_t* ids, int64_t st, int64_t sc, int64_t T,

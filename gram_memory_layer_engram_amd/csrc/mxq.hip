@@ -14,6 +14,7 @@
 // rows then never reach HBM. All of it is integer work on the bf16 bit patterns plus one exact
 // power-of-two multiply, so codes are reproducible bit for bit.
 #include "common.h"
+#include "fp8_table.h"
 #include "mx_rule.h"
 
 namespace engram {
@@ -38,9 +39,12 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(
 }
 
 // Row gather fused with the quantizer: block b of token t is 32 elements of
-// staged row c = (b*32) / head_dim, so the bf16 rows are never written.
+// staged row c = (b*32) / head_dim, so the bf16 rows are never written. With
+// an fp8 table (scales != nullptr) the block is dequantized to bf16 first
+// (fp8_table.h), then quantized by the same MX rule.
+template <bool FP8>
 __global__ __launch_bounds__(256) void gather_quantize_kernel(
-    const uint4* __restrict__ table, int64_t num_rows, int head_dim,
+    const uint4* __restrict__ table, const uint8_t* __restrict__ scales, int64_t num_rows, int head_dim,
     const int32_t* __restrict__ ids, int64_t st, int64_t sc, int n_cols,
     int64_t nblocks, uint4* __restrict__ xq, uint8_t* __restrict__ xs,
     int32_t* __restrict__ err) {
@@ -54,11 +58,18 @@ __global__ __launch_bounds__(256) void gather_quantize_kernel(
   const int64_t id = ids[t * st + (int64_t)c * sc];
   uint32_t w[16], packed[8];
   if (id >= 0 && id < num_rows) {
-    const uint4* src = table + (id * head_dim + part * 32) / 8;
+    if constexpr (FP8) {
+      const int64_t blk = id * bpr + part;
+      const uint4 c0 = table[blk * 2], c1 = table[blk * 2 + 1];
+      const uint32_t cw[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+      fp8_block_to_bf16(cw, scales[blk], w);
+    } else {
+      const uint4* src = table + (id * head_dim + part * 32) / 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint4 v = src[i];
-      w[4 * i + 0] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+      for (int i = 0; i < 4; ++i) {
+        const uint4 v = src[i];
+        w[4 * i + 0] = v.x; w[4 * i + 1] = v.y; w[4 * i + 2] = v.z; w[4 * i + 3] = v.w;
+      }
     }
   } else {
 #pragma unroll
@@ -73,14 +84,17 @@ __global__ __launch_bounds__(256) void gather_quantize_kernel(
 
 }  // namespace
 
-hipError_t launch_gather_quantize(const void* table, int64_t num_rows, int head_dim,
-                                  const int32_t* ids, int64_t st, int64_t sc, int64_t T,
-                                  int n_cols, uint8_t* xq, uint8_t* xs, int32_t* err,
-                                  hipStream_t s) {
+hipError_t launch_gather_quantize(const void* table, const uint8_t* table_scales, int64_t num_rows,
+                                  int head_dim, const int32_t* ids, int64_t st, int64_t sc, int64_t T,
+                                  int n_cols, uint8_t* xq, uint8_t* xs, int32_t* err, hipStream_t s) {
   const int64_t nblocks = T * n_cols * (head_dim / 32);
   const int grid = (int)((nblocks + 255) / 256);
-  hipLaunchKernelGGL(gather_quantize_kernel, dim3(grid), dim3(256), 0, s, (const uint4*)table,
-                     num_rows, head_dim, ids, st, sc, n_cols, nblocks, (uint4*)xq, xs, err);
+  if (table_scales)
+    hipLaunchKernelGGL(gather_quantize_kernel<true>, dim3(grid), dim3(256), 0, s, (const uint4*)table,
+                       table_scales, num_rows, head_dim, ids, st, sc, n_cols, nblocks, (uint4*)xq, xs, err);
+  else
+    hipLaunchKernelGGL(gather_quantize_kernel<false>, dim3(grid), dim3(256), 0, s, (const uint4*)table,
+                       nullptr, num_rows, head_dim, ids, st, sc, n_cols, nblocks, (uint4*)xq, xs, err);
   return hipGetLastError();
 }
 

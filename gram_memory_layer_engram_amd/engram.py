@@ -37,6 +37,7 @@ class ForwardArgs(ctypes.Structure):
         ("T", _i64), ("hc", _i32), ("dim", _i32), ("n_cols", _i32), ("head_dim", _i32),
         ("eps", _f32), ("clamp", _f32),
         ("out", _vp), ("gate_out", _vp), ("err_flag", _vp),
+        ("table_scales", _vp),
     ]
 
 
@@ -44,6 +45,7 @@ EXPORTS = {
     "engram_abi_version": (_i32, []),
     "engram_status_string": (ctypes.c_char_p, [_i32]),
     "engram_lookup": (_i32, [_vp, _i64, _i32, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
+    "engram_lookup_fp8": (_i32, [_vp, _vp, _i64, _i32, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
     "engram_mx_quantize": (_i32, [_vp, _i64, _i32, _vp, _vp, _vp]),
     "engram_wkv_workspace_size": (_sz, [_i64, _i32, _i32, _i32]),
     "engram_wkv": (_i32, [_vp, _i64, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _sz, _vp]),
@@ -120,6 +122,29 @@ def lookup(table: torch.Tensor, hash_ids: torch.Tensor, rows_out: torch.Tensor |
     return rows_out
 
 
+def lookup_fp8(table_codes: torch.Tensor, table_scales: torch.Tensor, hash_ids: torch.Tensor,
+               rows_out: torch.Tensor | None = None, err_flag: torch.Tensor | None = None) -> torch.Tensor:
+    """rows[t, c, :] = bf16(e4m3(codes[id]) * 2^(scales[id, j/32] - 127)), id = hash_ids[t, c]."""
+    L = load_library()
+    _dense(table_codes, "table_codes")
+    _dense(table_scales, "table_scales")
+    T, C = hash_ids.shape
+    hd = table_codes.shape[1]
+    if hash_ids.dtype != torch.int32:
+        raise ValueError("hash_ids must be int32")
+    if table_codes.dtype != torch.uint8 or table_scales.dtype != torch.uint8:
+        raise ValueError("fp8 table: uint8 codes and uint8 scale bytes")
+    if tuple(table_scales.shape) != (table_codes.shape[0], hd // 32):
+        raise ValueError("table_scales must be [num_rows, head_dim / 32]")
+    if rows_out is None:
+        rows_out = torch.empty((T, C, hd), dtype=torch.bfloat16, device=table_codes.device)
+    _dense(rows_out, "rows_out")
+    _check(L.engram_lookup_fp8(_ptr(table_codes), _ptr(table_scales), table_codes.shape[0], hd,
+                               _ptr(hash_ids), hash_ids.stride(0), hash_ids.stride(1), T, C,
+                               _ptr(rows_out), _ptr(err_flag), _stream()))
+    return rows_out
+
+
 def mx_quantize(x: torch.Tensor, xq: torch.Tensor | None = None, xs: torch.Tensor | None = None):
     """bf16 [T, K] -> (e4m3fn codes uint8 [T, K], E8M0 bytes uint8 [T, K/32])."""
     L = load_library()
@@ -178,7 +203,7 @@ def gate(hidden: torch.Tensor, kv: torch.Tensor, q_weight: torch.Tensor, k_weigh
 
 
 def forward_args(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask,
-                 eps, clamp, out, gate_out=None, err_flag=None) -> ForwardArgs:
+                 eps, clamp, out, gate_out=None, err_flag=None, table_scales=None) -> ForwardArgs:
     T, hc, dim = hidden.shape
     a = ForwardArgs()
     a.table = _ptr(table); a.num_rows = table.shape[0]
@@ -192,6 +217,11 @@ def forward_args(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token
     a.n_cols = hash_ids.shape[1]; a.head_dim = table.shape[1]
     a.eps = eps; a.clamp = clamp
     a.out = _ptr(out); a.gate_out = _ptr(gate_out); a.err_flag = _ptr(err_flag)
+    if table_scales is not None:
+        _dense(table_scales, "table_scales")
+        if table.dtype != torch.uint8 or tuple(table_scales.shape) != (table.shape[0], table.shape[1] // 32):
+            raise ValueError("fp8 table: uint8 codes [rows, hd] and scales [rows, hd / 32]")
+    a.table_scales = _ptr(table_scales)
     return a
 
 
@@ -201,9 +231,10 @@ def forward_workspace_size(args: ForwardArgs) -> int:
 
 def forward(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask=None,
             eps=1e-6, clamp=1e-6, out=None, gate_out=None, err_flag=None, workspace=None,
-            single_launch=False):
+            single_launch=False, table_scales=None):
     """One Engram layer forward: lookup -> (MXFP8 quantize) -> wkv -> gate.
-    ``single_launch`` selects engram_forward_single_launch (decode shapes)."""
+    ``single_launch`` selects engram_forward_single_launch (decode shapes);
+    ``table_scales`` makes ``table`` an fp8 table (uint8 e4m3 codes)."""
     L = load_library()
     for t, n in ((table, "table"), (w, "w"), (hidden, "hidden"),
                  (q_weight, "q_weight"), (k_weight, "k_weight")):
@@ -211,7 +242,7 @@ def forward(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask
     if out is None:
         out = torch.empty_like(hidden)
     args = forward_args(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask,
-                        eps, clamp, out, gate_out, err_flag)
+                        eps, clamp, out, gate_out, err_flag, table_scales)
     need = L.engram_forward_workspace_size(ctypes.byref(args))
     if workspace is None and need:
         workspace = new_forward_workspace(need, hidden.device)
@@ -235,7 +266,7 @@ class ForwardPlan:
 
     def __init__(self, table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask=None,
                  eps=1e-6, clamp=1e-6, out=None, gate_out=None, err_flag=None, workspace=None,
-                 stream=None, single_launch=False):
+                 stream=None, single_launch=False, table_scales=None):
         L = load_library()
         for t, n in ((table, "table"), (w, "w"), (hidden, "hidden"),
                      (q_weight, "q_weight"), (k_weight, "k_weight")):
@@ -244,9 +275,9 @@ class ForwardPlan:
             out = torch.empty_like(hidden)
         self.out = out
         self._keep = (table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask, gate_out,
-                      err_flag)
+                      err_flag, table_scales)
         self.args = forward_args(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask,
-                                 eps, clamp, out, gate_out, err_flag)
+                                 eps, clamp, out, gate_out, err_flag, table_scales)
         need = L.engram_forward_workspace_size(ctypes.byref(self.args))
         if workspace is None and need:
             workspace = new_forward_workspace(need, hidden.device)

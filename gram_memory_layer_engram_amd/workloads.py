@@ -139,7 +139,7 @@ def num_rows(wl: Workload) -> int:
 
 def _seeds(wl: Workload, variant: int) -> list[int]:
     ss = np.random.SeedSequence([SEED_BASE, wl.cfg_id, variant])
-    return [int(c.generate_state(1, dtype=np.uint64)[0] & 0x7FFFFFFFFFFFFFFF) for c in ss.spawn(9)]
+    return [int(c.generate_state(1, dtype=np.uint64)[0] & 0x7FFFFFFFFFFFFFFF) for c in ss.spawn(11)]
 
 
 def _gen(device, seed):
@@ -159,6 +159,24 @@ def make_table(wl: Workload, device="cpu", variant: int = 0) -> torch.Tensor:
         x = torch.randn((r1 - r0, wl.head_dim), generator=g, device=device, dtype=torch.float32)
         table[r0:r1] = (x * 0.02).to(torch.bfloat16)
     return table
+
+
+def make_table_fp8(wl: Workload, device="cpu", variant: int = 0):
+    """An fp8 table of the workload's shape: (e4m3fn codes as uint8
+    ``[rows, head_dim]``, ue8m0 bytes ``[rows, head_dim / 32]``). Codes are
+    N(0, 1) cast to e4m3fn, scale bytes 127 + U{-12 .. -5}, so element values
+    have the magnitude of the bf16 tables' N(0, 0.02). 2**20-row chunks."""
+    R = num_rows(wl)
+    s = _seeds(wl, variant)
+    g, gs = _gen(device, s[9]), _gen(device, s[10])
+    codes = torch.empty((R, wl.head_dim), dtype=torch.uint8, device=device)
+    chunk = 1 << 20
+    for r0 in range(0, R, chunk):
+        r1 = min(R, r0 + chunk)
+        x = torch.randn((r1 - r0, wl.head_dim), generator=g, device=device, dtype=torch.float32)
+        codes[r0:r1] = x.to(torch.float8_e4m3fn).view(torch.uint8)
+    scales = (127 + torch.randint(-12, -4, (R, wl.head_dim // 32), generator=gs, device=device)).to(torch.uint8)
+    return codes, scales
 
 
 def make_ids(wl: Workload, T: int | None = None, variant: int = 0) -> np.ndarray:

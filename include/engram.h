@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define ENGRAM_ABI_VERSION 1
+#define ENGRAM_ABI_VERSION 2
 
 /* Status codes. */
 enum {
@@ -77,6 +77,27 @@ int engram_lookup(const void* table, int64_t num_rows, int32_t head_dim,
                   const int32_t* hash_ids, int64_t ids_stride_t,
                   int64_t ids_stride_c, int64_t T, int32_t n_cols,
                   void* rows_out, int32_t* err_flag, void* stream);
+
+/*
+ * engram_lookup_fp8 -- the row gather from an fp8 table, dequantized to bf16.
+ *   [P-common] ParallelEngramEmbedding (docstring, __init__, lookup): the
+ *   table is float8_e4m3fn [rows, dim] with one uint8 ue8m0 scale per row and
+ *   32 elements (weight_scale_inv [rows, dim / 32]); rows stay fp8 and are
+ *   dequantized on lookup:
+ *     rows_out[t, c, j] = bf16_rne(e4m3(codes[id, j]) * 2^(scales[id, j/32] - 127))
+ *   with id = hash_ids[t * ids_stride_t + c * ids_stride_c] (scale byte 255
+ *   is NaN; products beyond the bf16 range become inf).
+ *
+ *   table_codes   uint8 e4m3fn codes [num_rows, head_dim], 16-byte aligned.
+ *   table_scales  uint8 ue8m0 bytes [num_rows, head_dim / 32].
+ *   Other arguments, the error flag and the errors as engram_lookup;
+ *   head_dim must be a multiple of 32 (<= 1024), else ENGRAM_EUNSUPPORTED.
+ */
+int engram_lookup_fp8(const void* table_codes, const uint8_t* table_scales,
+                      int64_t num_rows, int32_t head_dim,
+                      const int32_t* hash_ids, int64_t ids_stride_t,
+                      int64_t ids_stride_c, int64_t T, int32_t n_cols,
+                      void* rows_out, int32_t* err_flag, void* stream);
 
 /*
  * engram_mx_quantize -- MXFP8 quantization of bf16 activations.
@@ -184,6 +205,10 @@ typedef struct engram_forward_args {
   void* out;               /* bf16 [T, hc, dim] */
   float* gate_out;         /* optional fp32 [T, hc] */
   int32_t* err_flag;       /* optional int32 device flag, bits above */
+  const uint8_t* table_scales; /* NULL: `table` is bf16. Else `table` holds
+                                  e4m3 codes and these are its ue8m0 bytes
+                                  [num_rows, head_dim / 32], as in
+                                  engram_lookup_fp8 (head_dim % 32 == 0) */
 } engram_forward_args;
 
 size_t engram_forward_workspace_size(const engram_forward_args* a);
@@ -197,9 +222,9 @@ int engram_forward(const engram_forward_args* a, void* workspace,
  *   the split of [P-rocm] _engram_gate_partials_kernel /
  *   _engram_gate_finish_kernel (one shard). Same arguments, workspace size
  *   and results (to rounding of the gate's sums) as engram_forward.
- *   Supported: w_format ENGRAM_W_MXFP8, 1 <= T <= 64, K % 1024 == 0,
- *   head_dim % 32 == 0, dim % 16 == 0, T*K <= 128 KiB; else
- *   ENGRAM_EUNSUPPORTED.
+ *   Supported: w_format ENGRAM_W_MXFP8, bf16 table (table_scales NULL),
+ *   1 <= T <= 64, K % 1024 == 0, head_dim % 32 == 0, dim % 16 == 0,
+ *   T*K <= 128 KiB; else ENGRAM_EUNSUPPORTED.
  *   Its workgroups coordinate through flags in the first 64 KiB of the
  *   workspace:
  *     - those bytes must be zero before the first call on a workspace

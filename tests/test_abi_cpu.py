@@ -75,7 +75,7 @@ def test_forward_args_layout_matches_c():
 
 
 def test_status_strings_and_version(lib):
-    assert lib.engram_abi_version() == 1
+    assert lib.engram_abi_version() == 2
     assert lib.engram_status_string(0) == b"ok"
     assert lib.engram_status_string(1) == b"invalid argument"
     assert lib.engram_status_string(2) == b"unsupported shape"
@@ -101,6 +101,11 @@ def test_validation_answers_before_any_launch(lib):
     # misaligned pointers are refused (never dereferenced)
     assert lib.engram_gate(0x1002, 0x2000, 0x3000, 0x4000, None, 4, 4, 4096, 1e-6, 1e-6, 0x5000,
                            None, None) == 1
+    # fp8 tables: head_dim a multiple of 32, scales required
+    assert lib.engram_lookup_fp8(None, None, 10, 128, None, 16, 1, 0, 16, None, None, None) == 0
+    assert lib.engram_lookup_fp8(0x1000, 0x2000, 10, 48, 0x3000, 16, 1, 4, 16, 0x4000, None, None) == 2
+    assert lib.engram_lookup_fp8(0x1000, None, 10, 128, 0x3000, 16, 1, 4, 16, 0x4000, None, None) == 1
+    assert lib.engram_lookup_fp8(0x1008, 0x2000, 10, 128, 0x3000, 16, 1, 4, 16, 0x4000, None, None) == 1
 
 
 def test_workspace_sizes(lib):

@@ -162,6 +162,98 @@ def test_lookup_shapes(hd, T):
 # -------------------------------------------------------------- quantize --
 
 
+# ---------------------------------------------------------- fp8 tables --
+
+
+def _fp8_edge_table():
+    """Every e4m3 code (NaN codes included) in rows of 256, under scale
+    bytes that reach the ends of the bf16 range: 0..3 (subnormal floor),
+    ordinary bytes, 246 and 254 (top binade, overflow), 255 (NaN)."""
+    byte_list = [0, 1, 2, 3, 100, 119, 120, 127, 130, 140, 200, 246, 250, 254, 255]
+    R = len(byte_list) * 4
+    codes = np.tile(np.arange(256, dtype=np.uint8), (R, 1))
+    rng = np.random.default_rng(44)
+    for r in range(R):                       # each row its own code order
+        codes[r] = rng.permutation(codes[r])
+    scales = np.empty((R, 8), np.uint8)
+    for r in range(R):
+        scales[r] = [byte_list[(r + j) % len(byte_list)] for j in range(8)]
+    return codes, scales
+
+
+def test_lookup_fp8_bit_exact_over_all_codes_and_scale_edges():
+    E = _E()
+    codes, scales = _fp8_edge_table()
+    R = codes.shape[0]
+    rng = np.random.default_rng(45)
+    ids = rng.integers(0, R, size=(37, 5)).astype(np.int32)
+    ids[3, 2] = R          # out of range: zero row + flag
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    rows = E.lookup_fp8(torch.from_numpy(codes).to(DEV), torch.from_numpy(scales).to(DEV),
+                        torch.from_numpy(ids).to(DEV), err_flag=err)
+    ref, ref_err = o.gather_rows_fp8(codes, scales, ids)
+    torch.cuda.synchronize()
+    assert ref_err and int(err.item()) == 1
+    assert np.array_equal(bits(rows), ref)
+
+
+@pytest.mark.parametrize("name", ["mid", "prefill"])
+def test_lookup_fp8_workload_tables(name):
+    """The workload's table shape and id distribution (uniform / Zipf) in fp8,
+    strided ids view; sampled tokens bit-exact against the oracle."""
+    E = _E()
+    wl = W.WORKLOADS[name]
+    _say(f"fp8 table {name}")
+    codes, scales = W.make_table_fp8(wl, DEV)
+    ids_full = torch.from_numpy(np.stack([W.make_ids(wl)] * 2, axis=1)).to(DEV)   # [T, 2, C]
+    ids = ids_full[:, 1, :]                                                         # strided view
+    rows = E.lookup_fp8(codes, scales, ids)
+    toks = sample_tokens(wl.T, SAMPLE, seed=11)
+    idn = ids.cpu().numpy()[toks]
+    uniq, inv = np.unique(idn, return_inverse=True)
+    sel = torch.from_numpy(uniq).to(DEV).long()
+    ref, err = o.gather_rows_fp8(u8(codes[sel]), u8(scales[sel]), inv.reshape(idn.shape))
+    assert not err
+    assert np.array_equal(bits(rows)[toks], ref)
+    del codes, scales
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("wfmt,T", [("bf16", 70), ("mxfp8", 9), ("mxfp8", 300)])
+def test_forward_fp8_table(wfmt, T):
+    """engram_forward with an fp8 table: through the bf16 lookup + bf16 GEMM,
+    the fused gather+dequant+MX quantize + decode GEMV (T <= 64) and the
+    scaled GEMM (T > 64); against the oracle's forward on the same fp8 table."""
+    E = _E()
+    g = torch.Generator(device=DEV).manual_seed(2000 + T)
+    R, C, hd, dim, hc = 1999, 8, 128, 256, 2
+    K, N = C * hd, (hc + 1) * dim
+    codes = torch.randn((R, hd), generator=g, device=DEV).to(torch.float8_e4m3fn).view(torch.uint8)
+    scales = (127 + torch.randint(-12, -4, (R, hd // 32), generator=g, device=DEV)).to(torch.uint8)
+    ids = torch.randint(0, R, (T, C), generator=g, device=DEV, dtype=torch.int32)
+    if wfmt == "bf16":
+        w = (torch.randn((N, K), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+        ws = None
+    else:
+        w = torch.randn((N, K), generator=g, device=DEV).to(torch.float8_e4m3fn).view(torch.uint8)
+        ws = (127 + torch.randint(-8, 1, (N // 32, K // 32), generator=g, device=DEV)).to(torch.uint8)
+    hidden = torch.randn((T, hc, dim), generator=g, device=DEV).to(torch.bfloat16)
+    q = (1 + 0.1 * torch.randn((hc, dim), generator=g, device=DEV)).to(torch.bfloat16)
+    k = (1 + 0.1 * torch.randn((hc, dim), generator=g, device=DEV)).to(torch.bfloat16)
+    mask = torch.rand((T,), generator=g, device=DEV) > 0.1
+    gate_out = torch.empty((T, hc), dtype=torch.float32, device=DEV)
+    out = E.forward(codes, ids, w, ws, hidden, q, k, mask, gate_out=gate_out, table_scales=scales)
+    torch.cuda.synchronize()
+    ref = o.forward(u8(codes), ids.cpu().numpy(), bits(w) if ws is None else u8(w), None if ws is None else u8(ws),
+                    bits(hidden), bits(q), bits(k), mask.cpu().numpy(), 1e-6, 1e-6, table_scales=u8(scales))
+    assert_close(bf16_values(bits(out)), bf16_values(ref["out"]), *OUT_TOL, what="out")
+    assert np.max(np.abs(gate_out.cpu().numpy() - ref["gate"])) <= 2e-2
+    m = mask.cpu().numpy()
+    assert np.array_equal(bits(out)[~m], bits(hidden)[~m])
+    with pytest.raises(ValueError):   # the single launch takes bf16 tables only
+        E.forward(codes, ids, w, ws, hidden, q, k, mask, table_scales=scales, single_launch=True)
+
+
 @pytest.mark.parametrize("name", ["decode_t64", "long"])
 def test_mx_quantize_bit_exact(name):
     E = _E()
