@@ -81,21 +81,21 @@ def bench_prefill(steps, warmup):
                           inp["k"], None, wl.eps, wl.clamp, out)
     ws = torch.empty(E.forward_workspace_size(args), dtype=torch.uint8, device="cuda")
 
-    def fwd(_=0):
+    def fwd(_=0, gate_epilogue=False):
         E.forward(inp["table"], inp["ids"], inp["w"], None, inp["hidden"], inp["q"], inp["k"],
-                  None, wl.eps, wl.clamp, out=out, workspace=ws)
+                  None, wl.eps, wl.clamp, out=out, workspace=ws, gate_epilogue=gate_epilogue)
 
     for _ in range(warmup):
         fwd()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        fwd()
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / steps
 
-    # Per-kernel durations: the same three steps engram_forward enqueues,
-    # called one by one with events around each on the launch stream.
+    # Per-kernel durations, before the timed steps so that those start from
+    # the clocks and caches of a running loop: the default forward and the
+    # one with the GEMM's gate epilogue (keys never stored), alternated call
+    # by call so both see the same clocks; then the three steps
+    # engram_forward enqueues, called one by one. All event-timed on the
+    # launch stream.
+    t_both = _events_time(lambda i: fwd(i, i % 2 == 1), 2 * steps, stream)
+    t_fwd, t_fwd_epi = t_both[0::2], t_both[1::2]
     rows = torch.empty((wl.T, wl.C, wl.head_dim), dtype=torch.bfloat16, device="cuda")
     kv = torch.empty((wl.T, wl.N), dtype=torch.bfloat16, device="cuda")
     x = rows.view(wl.T, wl.K)
@@ -108,6 +108,16 @@ def bench_prefill(steps, warmup):
     t_wkv = _events_time(lambda i: E.wkv(x, inp["w"], kv=kv), steps, stream)
     t_gate = _events_time(lambda i: E.gate(inp["hidden"], kv, inp["q"], inp["k"], None, wl.eps,
                                            wl.clamp, out=out), steps, stream)
+
+    # the timed region: K forward steps between two synchronizations
+    fwd()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fwd()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
+
     # the same gather from the table stored as fp8 (e4m3 + ue8m0 per 32), dequantized on lookup
     del inp["table"]
     torch.cuda.empty_cache()
@@ -117,7 +127,8 @@ def bench_prefill(steps, warmup):
     for _ in range(warmup):
         L.engram_lookup_fp8(*look8)
     t_lookup8 = _events_time(lambda i: L.engram_lookup_fp8(*look8), steps, stream)
-    return wl, dt, {"lookup": t_lookup, "wkv": t_wkv, "gate": t_gate, "lookup_fp8": t_lookup8}
+    return wl, dt, {"lookup": t_lookup, "wkv": t_wkv, "gate": t_gate, "lookup_fp8": t_lookup8,
+                    "forward": t_fwd, "forward_gate_epilogue": t_fwd_epi}
 
 
 def bench_decode(steps, warmup, copies=16):
@@ -278,6 +289,8 @@ def main():
         "wkv_us": round(avg["wkv"] * 1e3, 2), "wkv_us_median": round(med["wkv"] * 1e3, 2),
         "gate_us": round(avg["gate"] * 1e3, 2),
         "gate_GBs": round(gate_bytes / (avg["gate"] * 1e-3) / 1e9, 1),
+        "forward_us_events": round(avg["forward"] * 1e3, 2),
+        "forward_gate_epilogue_us_events": round(avg["forward_gate_epilogue"] * 1e3, 2),
     }
 
     dwl, ddt, dkt = bench_decode(max(a.steps, 100), a.warmup)

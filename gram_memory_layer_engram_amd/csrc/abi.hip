@@ -60,27 +60,30 @@ int check_wkv(const void* x, int64_t T, int32_t K, const void* w,
 }
 
 // MXFP8 projection from already-quantized activations: decode GEMV for small
-// T, tiled scaled-MFMA GEMM otherwise.
+// T (which stores kv; `ep` is for the tiled GEMM only), tiled scaled-MFMA
+// GEMM otherwise.
 hipError_t run_mx_projection(const uint8_t* xq, const uint8_t* xs, int64_t T, int32_t K,
                              const void* w, const uint8_t* w_scales, int32_t N, void* kv,
-                             hipStream_t s) {
+                             hipStream_t s, const GateEpi& ep) {
   return gemv_mxfp8_supported(T, K)
              ? launch_gemv_mxfp8(xq, xs, T, K, (const uint8_t*)w, w_scales, N, kv, s)
-             : launch_gemm_mxfp8(xq, xs, T, K, (const uint8_t*)w, w_scales, N, kv, s);
+             : launch_gemm_mxfp8(xq, xs, T, K, (const uint8_t*)w, w_scales, N, kv, s, ep);
 }
+
+constexpr GateEpi kPlainStore{nullptr, nullptr, nullptr, nullptr, nullptr, 0, 0};
 
 // Enqueue the projection given a workspace already checked to be large enough.
 int run_wkv(const void* x, int64_t T, int32_t K, const void* w,
             const uint8_t* w_scales, int32_t w_format, int32_t N, void* kv,
-            void* workspace, hipStream_t s) {
+            void* workspace, hipStream_t s, const GateEpi& ep = kPlainStore) {
   if (T == 0) return ENGRAM_OK;
   if (w_format == ENGRAM_W_BF16)
-    return hip_status(launch_gemm_bf16(x, T, K, w, N, kv, s));
+    return hip_status(launch_gemm_bf16(x, T, K, w, N, kv, s, ep));
   uint8_t* xq = (uint8_t*)workspace;
   uint8_t* xs = xq + round_up((size_t)T * K);
   hipError_t e = launch_mx_quantize(x, T, K, xq, xs, s);
   if (e != hipSuccess) return ENGRAM_EHIP;
-  return hip_status(run_mx_projection(xq, xs, T, K, w, w_scales, N, kv, s));
+  return hip_status(run_mx_projection(xq, xs, T, K, w, w_scales, N, kv, s, ep));
 }
 
 int check_gate(const void* hidden, const void* kv, const void* q, const void* k,
@@ -220,7 +223,7 @@ size_t engram_forward_workspace_size(const engram_forward_args* a) {
 // Shared argument checks of the two forward entry points; sets K and N.
 int check_forward(const engram_forward_args* a, void* workspace, size_t workspace_bytes, int32_t* K,
                   int32_t* N) {
-  if (!a) return ENGRAM_EINVAL;
+  if (!a || (a->options & ~ENGRAM_FORWARD_GATE_EPILOGUE)) return ENGRAM_EINVAL;
   const int64_t K64 = (int64_t)a->n_cols * a->head_dim;
   const int64_t N64 = (int64_t)(a->hc + 1) * a->dim;
   if (K64 > INT32_MAX || N64 > INT32_MAX) return ENGRAM_EUNSUPPORTED;
@@ -253,6 +256,18 @@ int engram_forward(const engram_forward_args* a, void* workspace,
   void* rows = ws;
   void* kv = ws + round_up((size_t)a->T * K * 2);
   void* mx = (uint8_t*)kv + round_up((size_t)a->T * N * 2);
+  // With ENGRAM_FORWARD_GATE_EPILOGUE, when a tiled GEMM runs and a
+  // 256-column tile lies inside one key block (dim % 256 == 0), its epilogue
+  // turns key tiles into the gate's partial sums and stores only the value:
+  // kv's keys never reach HBM. The value and partials take kv's place in the
+  // workspace.
+  const bool tiled = a->w_format == ENGRAM_W_BF16 || !gemv_mxfp8_supported(a->T, K);
+  const bool epi = (a->options & ENGRAM_FORWARD_GATE_EPILOGUE) && tiled && a->dim % 256 == 0;
+  uint16_t* value = (uint16_t*)kv;
+  float2* part = (float2*)((uint8_t*)kv + round_up((size_t)a->T * a->dim * 2));
+  const GateEpi ep = epi ? GateEpi{(const uint16_t*)a->hidden, (const uint16_t*)a->q_weight,
+                                   (const uint16_t*)a->k_weight, value, part, a->hc, a->dim}
+                         : kPlainStore;
   hipError_t e;
   if (a->w_format == ENGRAM_W_MXFP8 && a->head_dim % 32 == 0) {
     // the gather feeds the quantizer directly: bf16 staged rows never reach HBM
@@ -261,7 +276,7 @@ int engram_forward(const engram_forward_args* a, void* workspace,
     e = launch_gather_quantize(a->table, a->table_scales, a->num_rows, a->head_dim, a->hash_ids,
                                a->ids_stride_t, a->ids_stride_c, a->T, a->n_cols, xq, xs, a->err_flag, s);
     if (e != hipSuccess) return ENGRAM_EHIP;
-    e = run_mx_projection(xq, xs, a->T, K, a->w, a->w_scales, N, kv, s);
+    e = run_mx_projection(xq, xs, a->T, K, a->w, a->w_scales, N, kv, s, ep);
     if (e != hipSuccess) return ENGRAM_EHIP;
   } else {
     e = a->table_scales
@@ -270,11 +285,13 @@ int engram_forward(const engram_forward_args* a, void* workspace,
             : launch_lookup(a->table, a->num_rows, a->head_dim, a->hash_ids, a->ids_stride_t,
                             a->ids_stride_c, a->T, a->n_cols, rows, a->err_flag, s);
     if (e != hipSuccess) return ENGRAM_EHIP;
-    st = run_wkv(rows, a->T, K, a->w, a->w_scales, a->w_format, N, kv, mx, s);
+    st = run_wkv(rows, a->T, K, a->w, a->w_scales, a->w_format, N, kv, mx, s, ep);
     if (st != ENGRAM_OK) return st;
   }
-  e = launch_gate(a->hidden, kv, a->q_weight, a->k_weight, a->token_mask, a->T, a->hc,
-                  a->dim, a->eps, a->clamp, a->out, a->gate_out, s);
+  e = epi ? launch_gate_parts(a->hidden, value, part, a->token_mask, a->T, a->hc, a->dim, a->eps,
+                              a->clamp, a->out, a->gate_out, s)
+          : launch_gate(a->hidden, kv, a->q_weight, a->k_weight, a->token_mask, a->T, a->hc,
+                        a->dim, a->eps, a->clamp, a->out, a->gate_out, s);
   return hip_status(e);
 }
 

@@ -45,6 +45,12 @@ hipError_t launch_gate(const void* hidden, const void* kv, const void* q,
                        int dim, float eps, float clamp, void* out,
                        float* gate_out, hipStream_t s);
 
+// The gate from the prefill GEMM's epilogue: partials [hc, T, dim/256] and
+// value [T, dim] in place of kv.
+hipError_t launch_gate_parts(const void* hidden, const void* value, const float2* part,
+                             const uint8_t* mask, int64_t T, int hc, int dim, float eps,
+                             float clamp, void* out, float* gate_out, hipStream_t s);
+
 hipError_t launch_mx_quantize(const void* x, int64_t T, int K, uint8_t* xq,
                               uint8_t* xs, hipStream_t s);
 
@@ -60,12 +66,24 @@ hipError_t launch_lookup_fp8(const void* codes, const uint8_t* scales, int64_t n
                              const int32_t* ids, int64_t st, int64_t sc, int64_t T, int n_cols, void* out,
                              int32_t* err, hipStream_t s);
 
+// Optional epilogue of the prefill GEMMs: with hidden != nullptr the key
+// tiles become the gate's per-(copy, token) partial sums over each 256-column
+// tile and only the value columns are stored (dim % 256 == 0).
+struct GateEpi {
+  const uint16_t* hidden;   // [T, hc, dim]; nullptr: store kv [T, N]
+  const uint16_t* q;        // [hc, dim]
+  const uint16_t* k;        // [hc, dim]
+  uint16_t* value;          // [T, dim]
+  float2* part;             // [hc, T, dim/256]: (sum hidden*q*k*key, sum key^2)
+  int hc, dim;
+};
+
 hipError_t launch_gemm_bf16(const void* x, int64_t T, int K, const void* w,
-                            int N, void* kv, hipStream_t s);
+                            int N, void* kv, hipStream_t s, const GateEpi& ep);
 
 hipError_t launch_gemm_mxfp8(const uint8_t* xq, const uint8_t* xs, int64_t T,
                              int K, const uint8_t* w, const uint8_t* ws, int N,
-                             void* kv, hipStream_t s);
+                             void* kv, hipStream_t s, const GateEpi& ep);
 
 hipError_t launch_gemv_mxfp8(const uint8_t* xq, const uint8_t* xs, int64_t T,
                              int K, const uint8_t* w, const uint8_t* ws, int N,

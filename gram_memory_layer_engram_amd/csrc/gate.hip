@@ -11,6 +11,9 @@
 // ("vllm.models.deepseek_v4_1.common.engram", Engram.forward docstring:
 // masked positions pass through untouched).
 //
+// After the prefill GEMM's gate epilogue the kv-side sums arrive as
+// per-tile partials and only the value row is read (launch_gate_parts).
+//
 // Layout on MI355X: for large T one workgroup per token serves all hc copies,
 // so the value row (the last dim-wide block of the kv row) is read once per
 // token instead of once per copy; for small T the copies are split over
@@ -42,10 +45,14 @@ __device__ __forceinline__ float wave_sum(float v) {
 // (blockIdx.y picks the group): all of them in one workgroup when T is large
 // (the value row is read once per token), one copy per workgroup when T is
 // small (more workgroups in flight; the value row then comes from L2).
-template <int HC, int CH, int BS>
+// PARTS: the kv-side sums arrive as per-256-column-tile partials from the
+// prefill GEMM's epilogue (part [hc, T, tiles]) and `kv` is the value
+// [T, dim] alone; only the hidden side is summed here.
+template <int HC, int CH, int BS, bool PARTS>
 __global__ __launch_bounds__(BS) void gate_kernel(
     const uint4* __restrict__ hidden, const uint4* __restrict__ kv,
     const uint4* __restrict__ qw, const uint4* __restrict__ kw,
+    const float2* __restrict__ part, int tiles, int T,
     const uint8_t* __restrict__ mask, int hc_total, int dim8, float inv_dim,
     float rsqrt_dim, float eps, float clamp, uint4* __restrict__ out,
     float* __restrict__ gate_out) {
@@ -58,9 +65,8 @@ __global__ __launch_bounds__(BS) void gate_kernel(
   const int h0 = blockIdx.y * HC;
   const int tid = threadIdx.x;
   const uint4* hrow = hidden + (t * hc_total + h0) * dim8;
-  const uint4* kvrow = kv + t * (hc_total + 1) * dim8;
-  const uint4* vrow = kvrow + hc_total * dim8;
-  kvrow += h0 * dim8;
+  const uint4* kvrow = PARTS ? nullptr : kv + t * (hc_total + 1) * dim8 + h0 * dim8;
+  const uint4* vrow = PARTS ? kv + t * dim8 : kv + t * (hc_total + 1) * dim8 + hc_total * dim8;
   qw += h0 * dim8;
   kw += h0 * dim8;
   uint4* orow = out + (t * hc_total + h0) * dim8;
@@ -90,6 +96,16 @@ __global__ __launch_bounds__(BS) void gate_kernel(
     const int j = tid + c * BS;
     vreg[c] = j < dim8 ? vrow[j] : make_uint4(0, 0, 0, 0);
   }
+  if constexpr (PARTS) {
+    if (tid < tiles) {
+#pragma unroll
+      for (int h = 0; h < HC; ++h) {
+        const float2 p = part[((int64_t)(h0 + h) * T + t) * tiles + tid];
+        dt[h] = p.x;
+        ks[h] = p.y;
+      }
+    }
+  }
 
 #pragma unroll
   for (int h = 0; h < HC; ++h) {
@@ -98,20 +114,24 @@ __global__ __launch_bounds__(BS) void gate_kernel(
       const int j = tid + c * BS;
       if (j < dim8) {
         const uint4 hv = hrow[h * dim8 + j];
-        const uint4 kv8 = kvrow[h * dim8 + j];
-        const uint4 q8 = qw[h * dim8 + j];
-        const uint4 k8 = kw[h * dim8 + j];
         if constexpr (KEEP) hreg[h][c] = hv;
-        float a[8], b[8], qf[8], kf[8];
+        float a[8];
         unpack8(hv, a);
-        unpack8(kv8, b);
-        unpack8(q8, qf);
-        unpack8(k8, kf);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          hs[h] = fmaf(a[e], a[e], hs[h]);
-          ks[h] = fmaf(b[e], b[e], ks[h]);
-          dt[h] = fmaf(a[e] * qf[e] * kf[e], b[e], dt[h]);
+        for (int e = 0; e < 8; ++e) hs[h] = fmaf(a[e], a[e], hs[h]);
+        if constexpr (!PARTS) {
+          const uint4 kv8 = kvrow[h * dim8 + j];
+          const uint4 q8 = qw[h * dim8 + j];
+          const uint4 k8 = kw[h * dim8 + j];
+          float b[8], qf[8], kf[8];
+          unpack8(kv8, b);
+          unpack8(q8, qf);
+          unpack8(k8, kf);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            ks[h] = fmaf(b[e], b[e], ks[h]);
+            dt[h] = fmaf(a[e] * qf[e] * kf[e], b[e], dt[h]);
+          }
         }
       }
     }
@@ -174,37 +194,54 @@ __global__ __launch_bounds__(BS) void gate_kernel(
   }
 }
 
-template <int HC, int CH, int BS>
-hipError_t launch_t(const void* hidden, const void* kv, const void* q,
-                    const void* k, const uint8_t* mask, int64_t T, int hc_total, int dim,
-                    float eps, float clamp, void* out, float* gate_out,
-                    hipStream_t s) {
-  hipLaunchKernelGGL((gate_kernel<HC, CH, BS>), dim3((unsigned)T, hc_total / HC), dim3(BS), 0, s,
-                     (const uint4*)hidden, (const uint4*)kv, (const uint4*)q,
-                     (const uint4*)k, mask, hc_total, dim / 8, 1.0f / (float)dim,
-                     1.0f / sqrtf((float)dim), eps, clamp, (uint4*)out,
-                     gate_out);
+struct GateCall {
+  const void* hidden; const void* kv; const void* q; const void* k;
+  const float2* part; int tiles;
+  const uint8_t* mask; int64_t T; int hc_total; int dim; float eps, clamp;
+  void* out; float* gate_out;
+};
+
+template <int HC, int CH, int BS, bool PARTS>
+hipError_t launch_t(const GateCall& g, hipStream_t s) {
+  hipLaunchKernelGGL((gate_kernel<HC, CH, BS, PARTS>), dim3((unsigned)g.T, g.hc_total / HC), dim3(BS), 0, s,
+                     (const uint4*)g.hidden, (const uint4*)g.kv, (const uint4*)g.q, (const uint4*)g.k,
+                     g.part, g.tiles, (int)g.T, g.mask, g.hc_total, g.dim / 8, 1.0f / (float)g.dim,
+                     1.0f / sqrtf((float)g.dim), g.eps, g.clamp, (uint4*)g.out, g.gate_out);
   return hipGetLastError();
 }
 
-template <int HC>
-hipError_t launch_hc(const void* hidden, const void* kv, const void* q,
-                     const void* k, const uint8_t* mask, int64_t T, int hc_total, int dim,
-                     float eps, float clamp, void* out, float* gate_out,
-                     hipStream_t s) {
-  const int dim8 = dim / 8;
-  if (dim8 <= 64) return launch_t<HC, 1, 64>(hidden, kv, q, k, mask, T, hc_total, dim, eps, clamp, out, gate_out, s);
-  if (dim8 <= 128) return launch_t<HC, 1, 128>(hidden, kv, q, k, mask, T, hc_total, dim, eps, clamp, out, gate_out, s);
+template <int HC, bool PARTS>
+hipError_t launch_hc(const GateCall& g, hipStream_t s) {
+  const int dim8 = g.dim / 8;
+  if (dim8 <= 64) return launch_t<HC, 1, 64, PARTS>(g, s);
+  if (dim8 <= 128) return launch_t<HC, 1, 128, PARTS>(g, s);
   const int ch = (dim8 + 255) / 256;
   switch (ch) {
-    case 1: return launch_t<HC, 1, 256>(hidden, kv, q, k, mask, T, hc_total, dim, eps, clamp, out, gate_out, s);
-    case 2: return launch_t<HC, 2, 256>(hidden, kv, q, k, mask, T, hc_total, dim, eps, clamp, out, gate_out, s);
-    case 3: return launch_t<HC, 3, 256>(hidden, kv, q, k, mask, T, hc_total, dim, eps, clamp, out, gate_out, s);
-    case 4: return launch_t<HC, 4, 256>(hidden, kv, q, k, mask, T, hc_total, dim, eps, clamp, out, gate_out, s);
-    case 5: return launch_t<HC, 5, 256>(hidden, kv, q, k, mask, T, hc_total, dim, eps, clamp, out, gate_out, s);
-    case 6: return launch_t<HC, 6, 256>(hidden, kv, q, k, mask, T, hc_total, dim, eps, clamp, out, gate_out, s);
-    case 7: return launch_t<HC, 7, 256>(hidden, kv, q, k, mask, T, hc_total, dim, eps, clamp, out, gate_out, s);
-    case 8: return launch_t<HC, 8, 256>(hidden, kv, q, k, mask, T, hc_total, dim, eps, clamp, out, gate_out, s);
+    case 1: return launch_t<HC, 1, 256, PARTS>(g, s);
+    case 2: return launch_t<HC, 2, 256, PARTS>(g, s);
+    case 3: return launch_t<HC, 3, 256, PARTS>(g, s);
+    case 4: return launch_t<HC, 4, 256, PARTS>(g, s);
+    case 5: return launch_t<HC, 5, 256, PARTS>(g, s);
+    case 6: return launch_t<HC, 6, 256, PARTS>(g, s);
+    case 7: return launch_t<HC, 7, 256, PARTS>(g, s);
+    case 8: return launch_t<HC, 8, 256, PARTS>(g, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <bool PARTS>
+hipError_t dispatch(const GateCall& g, hipStream_t s) {
+  // Few tokens: one copy per workgroup, so T*hc workgroups share the work.
+  if (g.T * 2 < dev_info().num_cus && g.hc_total > 1) return launch_hc<1, PARTS>(g, s);
+  switch (g.hc_total) {
+    case 1: return launch_hc<1, PARTS>(g, s);
+    case 2: return launch_hc<2, PARTS>(g, s);
+    case 3: return launch_hc<3, PARTS>(g, s);
+    case 4: return launch_hc<4, PARTS>(g, s);
+    case 5: return launch_hc<5, PARTS>(g, s);
+    case 6: return launch_hc<6, PARTS>(g, s);
+    case 7: return launch_hc<7, PARTS>(g, s);
+    case 8: return launch_hc<8, PARTS>(g, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -215,20 +252,15 @@ hipError_t launch_gate(const void* hidden, const void* kv, const void* q,
                        const void* k, const uint8_t* mask, int64_t T, int hc,
                        int dim, float eps, float clamp, void* out,
                        float* gate_out, hipStream_t s) {
-  // Few tokens: one copy per workgroup, so T*hc workgroups share the work.
-  if (T * 2 < dev_info().num_cus && hc > 1)
-    return launch_hc<1>(hidden, kv, q, k, mask, T, hc, dim, eps, clamp, out, gate_out, s);
-  switch (hc) {
-    case 1: return launch_hc<1>(hidden, kv, q, k, mask, T, hc, dim, eps, clamp, out, gate_out, s);
-    case 2: return launch_hc<2>(hidden, kv, q, k, mask, T, hc, dim, eps, clamp, out, gate_out, s);
-    case 3: return launch_hc<3>(hidden, kv, q, k, mask, T, hc, dim, eps, clamp, out, gate_out, s);
-    case 4: return launch_hc<4>(hidden, kv, q, k, mask, T, hc, dim, eps, clamp, out, gate_out, s);
-    case 5: return launch_hc<5>(hidden, kv, q, k, mask, T, hc, dim, eps, clamp, out, gate_out, s);
-    case 6: return launch_hc<6>(hidden, kv, q, k, mask, T, hc, dim, eps, clamp, out, gate_out, s);
-    case 7: return launch_hc<7>(hidden, kv, q, k, mask, T, hc, dim, eps, clamp, out, gate_out, s);
-    case 8: return launch_hc<8>(hidden, kv, q, k, mask, T, hc, dim, eps, clamp, out, gate_out, s);
-    default: return hipErrorInvalidValue;
-  }
+  const GateCall g{hidden, kv, q, k, nullptr, 0, mask, T, hc, dim, eps, clamp, out, gate_out};
+  return dispatch<false>(g, s);
+}
+
+hipError_t launch_gate_parts(const void* hidden, const void* value, const float2* part,
+                             const uint8_t* mask, int64_t T, int hc, int dim, float eps,
+                             float clamp, void* out, float* gate_out, hipStream_t s) {
+  const GateCall g{hidden, value, hidden, hidden, part, dim / 256, mask, T, hc, dim, eps, clamp, out, gate_out};
+  return dispatch<true>(g, s);
 }
 
 }  // namespace engram

@@ -134,14 +134,22 @@ __device__ __forceinline__ void bare_barrier() { asm volatile("s_barrier" ::: "m
 #define SGB(mask, n) __builtin_amdgcn_sched_group_barrier(mask, n, 0)
 constexpr int SG_MFMA = 0x008, SG_VMEM = 0x010, SG_DSR = 0x100;
 
-// Write the block's accumulators to kv: stage the bf16 tile in LDS as
-// [token][n] (512-byte rows; 16-byte chunk c of row t at c ^ (t & 31)), then
-// store whole rows. The caller has drained its DMAs; LDS is free after the
-// first barrier here. Rows past T and columns past N are not written
-// (N % 4 == 0, so a row's last chunk may be half).
+// Write the block's accumulators: stage the bf16 tile in LDS as [token][n]
+// (512-byte rows; 16-byte chunk c of row t at c ^ (t & 31)), then go over
+// whole rows. The caller has drained its DMAs; LDS is free after the first
+// barrier here. Rows past T are not written.
+//  * plain (ep.hidden == nullptr): store the rows into kv [T, N] (N % 4 == 0,
+//    so a row's last chunk may be half);
+//  * gate epilogue (dim % 256 == 0, so a tile lies inside one key block or
+//    the value block): value tiles go to ep.value [T, dim]; key tiles are
+//    not stored but reduced, per token, to the gate's two kv-side sums over
+//    the tile's 256 columns, sum hidden*q*k*key and sum key^2 of the
+//    bf16-rounded keys ("vllm.models.deepseek_v41.amd.engram",
+//    _engram_gate_partials_kernel, at tile granularity), into
+//    ep.part[(h*T + t) * (dim/256) + tile].
 __device__ __forceinline__ void store_tile(f32x16 (&acc)[4][4], char* smem, uint16_t* __restrict__ kv,
                                            int T, int N, int t0, int n0, int wn, int wt, int lane,
-                                           int wave) {
+                                           int wave, const GateEpi& ep) {
   const int lrow = lane & 31, lhalf = lane >> 5;
   wait_lgkm0();
   bare_barrier();
@@ -163,16 +171,80 @@ __device__ __forceinline__ void store_tile(f32x16 (&acc)[4][4], char* smem, uint
   wait_lgkm0();
   bare_barrier();
   const int c = lane & 31;
-  const int n = n0 + c * 8;
+  auto lds_row = [&](int t) { return *reinterpret_cast<const uint4*>(smem + t * 512 + ((c ^ (t & 31)) << 4)); };
+  if (!ep.hidden) {
+    const int n = n0 + c * 8;
 #pragma unroll 4
+    for (int it = 0; it < 32; ++it) {
+      const int t = wave * 64 + it * 2 + (lane >> 5);
+      const uint4 v = lds_row(t);
+      if (t0 + t < T) {
+        uint16_t* dst = kv + (int64_t)(t0 + t) * N + n;
+        if (n + 8 <= N) *reinterpret_cast<uint4*>(dst) = v;
+        else if (n + 4 <= N) *reinterpret_cast<uint2*>(dst) = make_uint2(v.x, v.y);
+      }
+    }
+    return;
+  }
+  const int key_cols = ep.hc * ep.dim;
+  if (n0 >= key_cols) {
+    // value tile
+    const int d = n0 - key_cols + c * 8;
+#pragma unroll 4
+    for (int it = 0; it < 32; ++it) {
+      const int t = wave * 64 + it * 2 + (lane >> 5);
+      const uint4 v = lds_row(t);
+      if (t0 + t < T) *reinterpret_cast<uint4*>(ep.value + (int64_t)(t0 + t) * ep.dim + d) = v;
+    }
+    return;
+  }
+  // key tile of copy h, columns d0 .. d0+255 of that copy
+  const int h = n0 / ep.dim, d0 = n0 - h * ep.dim;
+  const int d = d0 + c * 8;
+  float qk[8];
+  {
+    const uint4 q8 = *reinterpret_cast<const uint4*>(ep.q + h * ep.dim + d);
+    const uint4 k8 = *reinterpret_cast<const uint4*>(ep.k + h * ep.dim + d);
+    const uint32_t qw[4] = {q8.x, q8.y, q8.z, q8.w}, kw[4] = {k8.x, k8.y, k8.z, k8.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      qk[2 * e] = bf16lo(qw[e]) * bf16lo(kw[e]);
+      qk[2 * e + 1] = bf16hi(qw[e]) * bf16hi(kw[e]);
+    }
+  }
+  const int tiles = ep.dim / 256, tile = d0 / 256;
+  // all 32 hidden pieces of this thread in flight at once (the accumulators
+  // are dead, their registers free), then the reductions
+  uint4 hid[32];
+#pragma unroll
   for (int it = 0; it < 32; ++it) {
     const int t = wave * 64 + it * 2 + (lane >> 5);
-    const uint4 v = *reinterpret_cast<const uint4*>(smem + t * 512 + ((c ^ (t & 31)) << 4));
-    if (t0 + t < T) {
-      uint16_t* dst = kv + (int64_t)(t0 + t) * N + n;
-      if (n + 8 <= N) *reinterpret_cast<uint4*>(dst) = v;
-      else if (n + 4 <= N) *reinterpret_cast<uint2*>(dst) = make_uint2(v.x, v.y);
+    hid[it] = make_uint4(0, 0, 0, 0);
+    if (t0 + t < T) hid[it] = *reinterpret_cast<const uint4*>(ep.hidden + ((int64_t)(t0 + t) * ep.hc + h) * ep.dim + d);
+  }
+#pragma unroll
+  for (int it = 0; it < 32; ++it) {
+    const int t = wave * 64 + it * 2 + (lane >> 5);
+    const bool live = t0 + t < T;
+    const uint4 kv8 = lds_row(t);
+    const uint4 h8 = hid[it];
+    const uint32_t kw[4] = {kv8.x, kv8.y, kv8.z, kv8.w}, hw[4] = {h8.x, h8.y, h8.z, h8.w};
+    float dt = 0.f, ks = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float k0 = bf16lo(kw[e]), k1 = bf16hi(kw[e]);
+      ks = fmaf(k0, k0, ks);
+      ks = fmaf(k1, k1, ks);
+      dt = fmaf(bf16lo(hw[e]) * qk[2 * e], k0, dt);
+      dt = fmaf(bf16hi(hw[e]) * qk[2 * e + 1], k1, dt);
     }
+    // the 32 lanes of a row, in a fixed order
+#pragma unroll
+    for (int off = 16; off >= 1; off >>= 1) {
+      dt += __shfl_xor(dt, off, 64);
+      ks += __shfl_xor(ks, off, 64);
+    }
+    if (c == 0 && live) ep.part[((int64_t)h * T + t0 + t) * tiles + tile] = make_float2(dt, ks);
   }
 }
 
@@ -181,7 +253,7 @@ __device__ __forceinline__ void store_tile(f32x16 (&acc)[4][4], char* smem, uint
 template <bool KTAIL>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_bf16_kernel(const uint16_t* __restrict__ x, int T, int K, const uint16_t* __restrict__ w,
-                      int N, uint16_t* __restrict__ kv, int tiles_n, int tiles_t) {
+                      int N, uint16_t* __restrict__ kv, int tiles_n, int tiles_t, GateEpi ep) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   int tn, tt;
   tile_of(blockIdx.x, tiles_n, tiles_t, tn, tt);
@@ -298,13 +370,13 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ x, int T, int K, const uint16
   }
   __builtin_amdgcn_sched_barrier(0);
   wait_vm<0>();   // the zero-fill DMAs of the last stages land before LDS is reused
-  store_tile(acc, smem, kv, T, N, t0, n0, wn, wt, lane, wave);
+  store_tile(acc, smem, kv, T, N, t0, n0, wn, wt, lane, wave, ep);
 }
 
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void gemm_mxfp8_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, int T, int K,
                        const uint8_t* __restrict__ w, const uint8_t* __restrict__ ws, int N,
-                       uint16_t* __restrict__ kv, int tiles_n, int tiles_t) {
+                       uint16_t* __restrict__ kv, int tiles_n, int tiles_t, GateEpi ep) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   int tn, tt;
   tile_of(blockIdx.x, tiles_n, tiles_t, tn, tt);
@@ -389,7 +461,7 @@ void gemm_mxfp8_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict
     __syncthreads();
   }
 
-  store_tile(acc, smem, kv, T, N, t0, n0, wn, wt, lane, wave);
+  store_tile(acc, smem, kv, T, N, t0, n0, wn, wt, lane, wave, ep);
 }
 
 hipError_t set_lds(const void* fn) {
@@ -399,7 +471,7 @@ hipError_t set_lds(const void* fn) {
 }  // namespace
 
 hipError_t launch_gemm_bf16(const void* x, int64_t T, int K, const void* w, int N, void* kv,
-                            hipStream_t s) {
+                            hipStream_t s, const GateEpi& ep) {
   const int tiles_n = (N + BM - 1) / BM;
   const int tiles_t = (int)((T + BN - 1) / BN);
   const dim3 grid(tiles_n * tiles_t), block(THREADS);
@@ -407,23 +479,23 @@ hipError_t launch_gemm_bf16(const void* x, int64_t T, int K, const void* w, int 
   if (K % 32 == 0) {
     if ((e = set_lds((const void*)gemm_bf16_kernel<false>)) != hipSuccess) return e;
     hipLaunchKernelGGL(gemm_bf16_kernel<false>, grid, block, LDS_BYTES, s, (const uint16_t*)x, (int)T, K,
-                       (const uint16_t*)w, N, (uint16_t*)kv, tiles_n, tiles_t);
+                       (const uint16_t*)w, N, (uint16_t*)kv, tiles_n, tiles_t, ep);
   } else {
     if ((e = set_lds((const void*)gemm_bf16_kernel<true>)) != hipSuccess) return e;
     hipLaunchKernelGGL(gemm_bf16_kernel<true>, grid, block, LDS_BYTES, s, (const uint16_t*)x, (int)T, K,
-                       (const uint16_t*)w, N, (uint16_t*)kv, tiles_n, tiles_t);
+                       (const uint16_t*)w, N, (uint16_t*)kv, tiles_n, tiles_t, ep);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_mxfp8(const uint8_t* xq, const uint8_t* xs, int64_t T, int K, const uint8_t* w,
-                             const uint8_t* ws, int N, void* kv, hipStream_t s) {
+                             const uint8_t* ws, int N, void* kv, hipStream_t s, const GateEpi& ep) {
   const int tiles_n = (N + BM - 1) / BM;
   const int tiles_t = (int)((T + BN - 1) / BN);
   hipError_t e = set_lds((const void*)gemm_mxfp8_kernel);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(gemm_mxfp8_kernel, dim3(tiles_n * tiles_t), dim3(THREADS), LDS_BYTES, s, xq, xs,
-                     (int)T, K, w, ws, N, (uint16_t*)kv, tiles_n, tiles_t);
+                     (int)T, K, w, ws, N, (uint16_t*)kv, tiles_n, tiles_t, ep);
   return hipGetLastError();
 }
 

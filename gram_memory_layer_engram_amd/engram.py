@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libengram.so")
 
 ENGRAM_OK, ENGRAM_EINVAL, ENGRAM_EUNSUPPORTED, ENGRAM_EHIP = 0, 1, 2, 3
 W_BF16, W_MXFP8 = 0, 1
+FORWARD_GATE_EPILOGUE = 1
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -37,7 +38,7 @@ class ForwardArgs(ctypes.Structure):
         ("T", _i64), ("hc", _i32), ("dim", _i32), ("n_cols", _i32), ("head_dim", _i32),
         ("eps", _f32), ("clamp", _f32),
         ("out", _vp), ("gate_out", _vp), ("err_flag", _vp),
-        ("table_scales", _vp),
+        ("table_scales", _vp), ("options", _i32),
     ]
 
 
@@ -203,7 +204,8 @@ def gate(hidden: torch.Tensor, kv: torch.Tensor, q_weight: torch.Tensor, k_weigh
 
 
 def forward_args(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask,
-                 eps, clamp, out, gate_out=None, err_flag=None, table_scales=None) -> ForwardArgs:
+                 eps, clamp, out, gate_out=None, err_flag=None, table_scales=None,
+                 gate_epilogue=False) -> ForwardArgs:
     T, hc, dim = hidden.shape
     a = ForwardArgs()
     a.table = _ptr(table); a.num_rows = table.shape[0]
@@ -222,6 +224,7 @@ def forward_args(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token
         if table.dtype != torch.uint8 or tuple(table_scales.shape) != (table.shape[0], table.shape[1] // 32):
             raise ValueError("fp8 table: uint8 codes [rows, hd] and scales [rows, hd / 32]")
     a.table_scales = _ptr(table_scales)
+    a.options = FORWARD_GATE_EPILOGUE if gate_epilogue else 0
     return a
 
 
@@ -231,10 +234,12 @@ def forward_workspace_size(args: ForwardArgs) -> int:
 
 def forward(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask=None,
             eps=1e-6, clamp=1e-6, out=None, gate_out=None, err_flag=None, workspace=None,
-            single_launch=False, table_scales=None):
+            single_launch=False, table_scales=None, gate_epilogue=False):
     """One Engram layer forward: lookup -> (MXFP8 quantize) -> wkv -> gate.
     ``single_launch`` selects engram_forward_single_launch (decode shapes);
-    ``table_scales`` makes ``table`` an fp8 table (uint8 e4m3 codes)."""
+    ``table_scales`` makes ``table`` an fp8 table (uint8 e4m3 codes);
+    ``gate_epilogue`` sets ENGRAM_FORWARD_GATE_EPILOGUE (the tiled GEMM
+    reduces key tiles to the gate's partial sums, keys never stored)."""
     L = load_library()
     for t, n in ((table, "table"), (w, "w"), (hidden, "hidden"),
                  (q_weight, "q_weight"), (k_weight, "k_weight")):
@@ -242,7 +247,7 @@ def forward(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask
     if out is None:
         out = torch.empty_like(hidden)
     args = forward_args(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask,
-                        eps, clamp, out, gate_out, err_flag, table_scales)
+                        eps, clamp, out, gate_out, err_flag, table_scales, gate_epilogue)
     need = L.engram_forward_workspace_size(ctypes.byref(args))
     if workspace is None and need:
         workspace = new_forward_workspace(need, hidden.device)
@@ -266,7 +271,7 @@ class ForwardPlan:
 
     def __init__(self, table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask=None,
                  eps=1e-6, clamp=1e-6, out=None, gate_out=None, err_flag=None, workspace=None,
-                 stream=None, single_launch=False, table_scales=None):
+                 stream=None, single_launch=False, table_scales=None, gate_epilogue=False):
         L = load_library()
         for t, n in ((table, "table"), (w, "w"), (hidden, "hidden"),
                      (q_weight, "q_weight"), (k_weight, "k_weight")):
@@ -277,7 +282,7 @@ class ForwardPlan:
         self._keep = (table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask, gate_out,
                       err_flag, table_scales)
         self.args = forward_args(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask,
-                                 eps, clamp, out, gate_out, err_flag, table_scales)
+                                 eps, clamp, out, gate_out, err_flag, table_scales, gate_epilogue)
         need = L.engram_forward_workspace_size(ctypes.byref(self.args))
         if workspace is None and need:
             workspace = new_forward_workspace(need, hidden.device)

@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define ENGRAM_ABI_VERSION 2
+#define ENGRAM_ABI_VERSION 3
 
 /* Status codes. */
 enum {
@@ -209,7 +209,25 @@ typedef struct engram_forward_args {
                                   e4m3 codes and these are its ue8m0 bytes
                                   [num_rows, head_dim / 32], as in
                                   engram_lookup_fp8 (head_dim % 32 == 0) */
+  int32_t options;         /* 0, or ENGRAM_FORWARD_GATE_EPILOGUE; other bits
+                              give ENGRAM_EINVAL */
 } engram_forward_args;
+
+/*
+ * ENGRAM_FORWARD_GATE_EPILOGUE -- engram_forward option. Where the projection
+ *   runs as a tiled GEMM (bf16 weights, or MXFP8 with T too large for the
+ *   decode GEMV) and dim % 256 == 0, the GEMM's epilogue reduces each
+ *   256-column key tile against hidden, q and k to the gate's per-tile sums
+ *   (sum key^2, sum hidden*q*k*key over the bf16-rounded keys: the partial /
+ *   finish split of [P-rocm] _engram_gate_partials_kernel /
+ *   _engram_gate_finish_kernel at tile granularity) and stores only the value,
+ *   so the keys never reach HBM. Elsewhere the option has no effect. Results
+ *   match the default path to the rounding of the gate's sums. On MI355X at
+ *   T 8192, dim 4096 both paths take the same time to within 1%: the
+ *   gate's hidden reads move into the compute-bound GEMM's epilogue, where
+ *   they stall it about as long as the key traffic they remove saves.
+ */
+#define ENGRAM_FORWARD_GATE_EPILOGUE 1
 
 size_t engram_forward_workspace_size(const engram_forward_args* a);
 int engram_forward(const engram_forward_args* a, void* workspace,

@@ -75,7 +75,7 @@ def test_forward_args_layout_matches_c():
 
 
 def test_status_strings_and_version(lib):
-    assert lib.engram_abi_version() == 2
+    assert lib.engram_abi_version() == 3
     assert lib.engram_status_string(0) == b"ok"
     assert lib.engram_status_string(1) == b"invalid argument"
     assert lib.engram_status_string(2) == b"unsupported shape"
@@ -118,6 +118,18 @@ def test_workspace_sizes(lib):
     a.T, a.hc, a.dim, a.n_cols, a.head_dim, a.w_format = 8192, 4, 4096, 16, 128, engram.W_BF16
     need = lib.engram_forward_workspace_size(ctypes.byref(a))
     assert need >= 8192 * 2048 * 2 + 8192 * 20480 * 2
+
+
+def test_forward_rejects_unknown_options(lib):
+    """Only ENGRAM_FORWARD_GATE_EPILOGUE is a known option bit; any other is
+    EINVAL before any argument is looked at or anything is launched."""
+    from gram_memory_layer_engram_amd import engram
+
+    for fn in (lib.engram_forward, lib.engram_forward_single_launch):
+        for bad in (2, 4, 1 | 8, -1):
+            a = engram.ForwardArgs()
+            a.options = bad
+            assert fn(ctypes.byref(a), None, 0, None) == 1
 
 
 # ------------------------------------------------------ input generator --

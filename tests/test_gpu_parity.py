@@ -519,6 +519,50 @@ def test_forward_small_hidden_engram_term_dominates():
     assert np.linalg.norm(delta_got - delta_ref) <= 2e-2 * np.linalg.norm(delta_ref)
 
 
+@pytest.mark.parametrize("wfmt,T,dim,hc", [("bf16", 300, 512, 3), ("bf16", 300, 136, 2), ("bf16", 1, 256, 1),
+                                           ("mxfp8", 257, 512, 2), ("mxfp8", 200, 160, 2)])
+def test_forward_gate_epilogue_and_plain_paths(wfmt, T, dim, hc):
+    """With gate_epilogue and dim % 256 == 0 the forward runs the GEMM's gate
+    epilogue (key tiles reduced to per-tile partials, only the value stored);
+    without it, or at other dims, kv is stored and the plain gate runs. Both
+    against the oracle, ragged token tiles, masked tokens; each path
+    bit-identical over two runs."""
+    E = _E()
+    g = torch.Generator(device=DEV).manual_seed(3000 + T + dim)
+    R, C, hd = 2503, 4, 128
+    K, N = C * hd, (hc + 1) * dim
+    table = (torch.randn((R, hd), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    ids = torch.randint(0, R, (T, C), generator=g, device=DEV, dtype=torch.int32)
+    if wfmt == "bf16":
+        w = (torch.randn((N, K), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+        ws = None
+    else:
+        w = torch.randn((N, K), generator=g, device=DEV).to(torch.float8_e4m3fn).view(torch.uint8)
+        ws = (127 + torch.randint(-8, 1, (N // 32, K // 32), generator=g, device=DEV)).to(torch.uint8)
+    hidden = torch.randn((T, hc, dim), generator=g, device=DEV).to(torch.bfloat16)
+    q = (1 + 0.1 * torch.randn((hc, dim), generator=g, device=DEV)).to(torch.bfloat16)
+    k = (1 + 0.1 * torch.randn((hc, dim), generator=g, device=DEV)).to(torch.bfloat16)
+    mask = torch.rand((T,), generator=g, device=DEV) > 0.15
+    ref = o.forward(bits(table), ids.cpu().numpy(), bits(w) if ws is None else u8(w),
+                    None if ws is None else u8(ws), bits(hidden), bits(q), bits(k), mask.cpu().numpy(),
+                    1e-6, 1e-6)
+    m = mask.cpu().numpy()
+    gates = []
+    for epi in (False, True):
+        gate_out = torch.empty((T, hc), dtype=torch.float32, device=DEV)
+        out = E.forward(table, ids, w, ws, hidden, q, k, mask, gate_out=gate_out, gate_epilogue=epi).clone()
+        out2 = E.forward(table, ids, w, ws, hidden, q, k, mask, gate_epilogue=epi)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), epi
+        assert_close(bf16_values(bits(out)), bf16_values(ref["out"]), *OUT_TOL, what=f"out epi={epi}")
+        assert np.max(np.abs(gate_out.cpu().numpy() - ref["gate"])) <= 2e-2, epi
+        assert np.array_equal(bits(out)[~m], bits(hidden)[~m]), epi
+        assert np.all(gate_out.cpu().numpy()[~m] == 0), epi
+        gates.append(gate_out.cpu().numpy())
+    # both paths see the same bf16 keys; only the order of the gate's sums differs
+    assert np.max(np.abs(gates[0] - gates[1])) <= 1e-3
+
+
 @pytest.mark.parametrize("T", [1, 5, 16, 17, 31, 32, 33, 64, 65])
 def test_forward_mxfp8_decode_paths_and_bad_ids(T):
     """K = 512 (not a multiple of 1024): T <= 64 runs the fused
