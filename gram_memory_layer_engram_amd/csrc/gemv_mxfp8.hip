@@ -59,6 +59,10 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_mxfp8_kernel(
   const int nsteps = K / 128;
   const int step0 = wave * SPW;
 
+  // Every load is issued before the first MFMA: weights, then activations.
+  // Each sits behind its own (uniform) bounds test, which also keeps the
+  // compiler from moving it next to its use; a padding token reloads token
+  // 0 (its MFMA column only feeds outputs that are not stored).
   uint4 wlo[RT][SPW], whi[RT][SPW];
   int wsc[RT][SPW];
 #pragma unroll
@@ -77,6 +81,24 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_mxfp8_kernel(
       }
     }
   }
+  uint4 xlo[NT][SPW], xhi[NT][SPW];
+  int xsc[NT][SPW];
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int t = j * 16 + r < T ? j * 16 + r : 0;
+    const uint8_t* xrow = xq + (int64_t)t * K;
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+      xlo[j][s] = xhi[j][s] = make_uint4(0, 0, 0, 0);
+      xsc[j][s] = 0;
+      if (step0 + s < nsteps) {
+        const int kbyte = (step0 + s) * 128 + 16 * g;
+        xlo[j][s] = *reinterpret_cast<const uint4*>(xrow + kbyte);
+        xhi[j][s] = *reinterpret_cast<const uint4*>(xrow + kbyte + 64);
+        xsc[j][s] = xs[(int64_t)t * kb + (step0 + s) * 4 + g];
+      }
+    }
+  }
 
   f32x4 acc[RT][NT];
 #pragma unroll
@@ -86,25 +108,14 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_mxfp8_kernel(
 
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
-    const int t = j * 16 + r;
-    const bool live = t < T;
-    const uint8_t* xrow = xq + (int64_t)(live ? t : 0) * K;
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
       if (step0 + s >= nsteps) break;  // uniform per wave
-      const int kbyte = (step0 + s) * 128 + 16 * g;
-      uint4 xlo = make_uint4(0, 0, 0, 0), xhi = make_uint4(0, 0, 0, 0);
-      int xsc = 0;
-      if (live) {
-        xlo = *reinterpret_cast<const uint4*>(xrow + kbyte);
-        xhi = *reinterpret_cast<const uint4*>(xrow + kbyte + 64);
-        xsc = xs[(int64_t)t * kb + (step0 + s) * 4 + g];
-      }
-      const i32x8 xb = cat(xlo, xhi);
+      const i32x8 xb = cat(xlo[j][s], xhi[j][s]);
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
         acc[rt][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            cat(wlo[rt][s], whi[rt][s]), xb, acc[rt][j], 0, 0, 0, wsc[rt][s], 0, xsc);
+            cat(wlo[rt][s], whi[rt][s]), xb, acc[rt][j], 0, 0, 0, wsc[rt][s], 0, xsc[j][s]);
     }
   }
 

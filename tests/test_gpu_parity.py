@@ -219,7 +219,7 @@ def test_lookup_fp8_workload_tables(name):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("wfmt,T", [("bf16", 70), ("mxfp8", 9), ("mxfp8", 300)])
+@pytest.mark.parametrize("wfmt,T", [("bf16", 70), ("mxfp8", 9), ("mxfp8", 64), ("mxfp8", 300)])
 def test_forward_fp8_table(wfmt, T):
     """engram_forward with an fp8 table: through the bf16 lookup + bf16 GEMM,
     the fused gather+dequant+MX quantize + decode GEMV (T <= 64) and the
@@ -563,15 +563,16 @@ def test_forward_gate_epilogue_and_plain_paths(wfmt, T, dim, hc):
     assert np.max(np.abs(gates[0] - gates[1])) <= 1e-3
 
 
+@pytest.mark.parametrize("C", [4, 3])
 @pytest.mark.parametrize("T", [1, 5, 16, 17, 31, 32, 33, 64, 65])
-def test_forward_mxfp8_decode_paths_and_bad_ids(T):
-    """K = 512 (not a multiple of 1024): T <= 64 runs the fused
-    gather+quantize launch, the decode GEMV and the gate kernel, 65 the
-    scaled-MFMA GEMM; all against the oracle, with one out-of-range id (zero
-    row + flag)."""
+def test_forward_mxfp8_decode_paths_and_bad_ids(T, C):
+    """T <= 64 runs the fused gather+quantize launch, the decode GEMV and the
+    gate kernel, T = 65 the scaled-MFMA GEMM; K = 512 gives every wave of the
+    GEMV its k steps, K = 384 leaves waves without any. All against the
+    oracle, with one out-of-range id (zero row + flag)."""
     E = _E()
-    g = torch.Generator(device=DEV).manual_seed(1000 + T)
-    R, C, hd, dim, hc = 3001, 4, 128, 256, 2
+    g = torch.Generator(device=DEV).manual_seed(1000 + T + 7 * C)
+    R, hd, dim, hc = 3001, 128, 256, 2
     K, N = C * hd, (hc + 1) * dim
     table = (torch.randn((R, hd), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
     ids = torch.randint(0, R, (T, C), generator=g, device=DEV, dtype=torch.int32)
