@@ -194,6 +194,129 @@ __global__ __launch_bounds__(BS) void gate_kernel(
   }
 }
 
+// The same gate when each thread owns exactly one 16-byte piece of every row
+// (BS == dim/8): no bounds tests, so every load of the workgroup -- the mask
+// byte, the value, the hidden and key rows, q, k or the partials -- is issued
+// before the first wait. (Behind per-piece bounds tests the compiler waits
+// after each group of four loads: eight dependent round trips per token.)
+// A masked token still reads its rows and then copies hidden.
+template <int HC, int BS, bool PARTS>
+__global__ __launch_bounds__(BS) void gate_exact_kernel(
+    const uint4* __restrict__ hidden, const uint4* __restrict__ kv,
+    const uint4* __restrict__ qw, const uint4* __restrict__ kw,
+    const float2* __restrict__ part, int tiles, int T,
+    const uint8_t* __restrict__ mask, int hc_total, float inv_dim,
+    float rsqrt_dim, float eps, float clamp, uint4* __restrict__ out,
+    float* __restrict__ gate_out) {
+  constexpr int NW = BS / 64, dim8 = BS;
+  __shared__ float red[NW][3 * HC];
+  __shared__ float gates[HC];
+
+  const int64_t t = blockIdx.x;
+  const int h0 = blockIdx.y * HC;
+  const int tid = threadIdx.x;
+  const uint4* hrow = hidden + (t * hc_total + h0) * dim8;
+  const uint4* kvrow = PARTS ? nullptr : kv + t * (hc_total + 1) * dim8 + h0 * dim8;
+  const uint4* vrow = PARTS ? kv + t * dim8 : kv + t * (hc_total + 1) * dim8 + hc_total * dim8;
+  uint4* orow = out + (t * hc_total + h0) * dim8;
+
+  const uint4 vv = vrow[tid];
+  uint4 hv[HC], k8[HC], qv[HC], kwv[HC];
+  float2 p[HC];
+#pragma unroll
+  for (int h = 0; h < HC; ++h) hv[h] = hrow[h * dim8 + tid];
+  if constexpr (!PARTS) {
+#pragma unroll
+    for (int h = 0; h < HC; ++h) {
+      k8[h] = kvrow[h * dim8 + tid];
+      qv[h] = qw[(h0 + h) * dim8 + tid];
+      kwv[h] = kw[(h0 + h) * dim8 + tid];
+    }
+  } else {
+    const int i = tid < tiles ? tid : 0;
+#pragma unroll
+    for (int h = 0; h < HC; ++h) p[h] = part[((int64_t)(h0 + h) * T + t) * tiles + i];
+  }
+  // the mask byte last (without a mask, hidden's first byte, ignored)
+  const uint8_t mbyte = *(mask ? mask + t : reinterpret_cast<const uint8_t*>(hrow));
+  __builtin_amdgcn_sched_barrier(0);
+
+  float hs[HC], ks[HC], dt[HC];
+#pragma unroll
+  for (int h = 0; h < HC; ++h) {
+    float a[8];
+    unpack8(hv[h], a);
+    hs[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) hs[h] = fmaf(a[e], a[e], hs[h]);
+    if constexpr (!PARTS) {
+      float b[8], qf[8], kf[8];
+      unpack8(k8[h], b);
+      unpack8(qv[h], qf);
+      unpack8(kwv[h], kf);
+      ks[h] = dt[h] = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        ks[h] = fmaf(b[e], b[e], ks[h]);
+        dt[h] = fmaf(a[e] * qf[e] * kf[e], b[e], dt[h]);
+      }
+    } else {
+      dt[h] = tid < tiles ? p[h].x : 0.f;
+      ks[h] = tid < tiles ? p[h].y : 0.f;
+    }
+  }
+
+  const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int h = 0; h < HC; ++h) {
+    const float s0 = wave_sum(hs[h]);
+    const float s1 = wave_sum(ks[h]);
+    const float s2 = wave_sum(dt[h]);
+    if (lane == 0) {
+      red[wave][3 * h + 0] = s0;
+      red[wave][3 * h + 1] = s1;
+      red[wave][3 * h + 2] = s2;
+    }
+  }
+  __syncthreads();
+  const bool active = mask == nullptr || mbyte != 0;
+  if (tid < HC) {
+    const int h = tid;
+    float s0 = 0.f, s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {  // fixed wave order
+      s0 += red[w][3 * h + 0];
+      s1 += red[w][3 * h + 1];
+      s2 += red[w][3 * h + 2];
+    }
+    const float hidden_rms = 1.0f / sqrtf(s0 * inv_dim + eps);
+    const float key_rms = 1.0f / sqrtf(s1 * inv_dim + eps);
+    const float d = s2 * hidden_rms * key_rms * rsqrt_dim;
+    float s = sqrtf(fmaxf(fabsf(d), clamp));
+    s = d < 0.0f ? -s : s;
+    const float g = 1.0f / (1.0f + expf(-s));
+    gates[h] = g;
+    if (gate_out) gate_out[t * hc_total + h0 + h] = active ? g : 0.0f;
+  }
+  __syncthreads();
+
+  float v[8];
+  unpack8(vv, v);
+#pragma unroll
+  for (int h = 0; h < HC; ++h) {
+    const float g = gates[h];
+    float a[8];
+    unpack8(hv[h], a);
+    uint4 o;
+    o.x = pack_bf16x2(fmaf(g, v[0], a[0]), fmaf(g, v[1], a[1]));
+    o.y = pack_bf16x2(fmaf(g, v[2], a[2]), fmaf(g, v[3], a[3]));
+    o.z = pack_bf16x2(fmaf(g, v[4], a[4]), fmaf(g, v[5], a[5]));
+    o.w = pack_bf16x2(fmaf(g, v[6], a[6]), fmaf(g, v[7], a[7]));
+    if (!active) o = hv[h];   // masked: hidden, bit for bit
+    orow[h * dim8 + tid] = o;
+  }
+}
+
 struct GateCall {
   const void* hidden; const void* kv; const void* q; const void* k;
   const float2* part; int tiles;
@@ -210,9 +333,34 @@ hipError_t launch_t(const GateCall& g, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int HC, int BS, bool PARTS>
+hipError_t launch_exact(const GateCall& g, hipStream_t s) {
+  hipLaunchKernelGGL((gate_exact_kernel<HC, BS, PARTS>), dim3((unsigned)g.T, g.hc_total / HC), dim3(BS), 0, s,
+                     (const uint4*)g.hidden, (const uint4*)g.kv, (const uint4*)g.q, (const uint4*)g.k,
+                     g.part, g.tiles, (int)g.T, g.mask, g.hc_total, 1.0f / (float)g.dim,
+                     1.0f / sqrtf((float)g.dim), g.eps, g.clamp, (uint4*)g.out, g.gate_out);
+  return hipGetLastError();
+}
+
 template <int HC, bool PARTS>
 hipError_t launch_hc(const GateCall& g, hipStream_t s) {
   const int dim8 = g.dim / 8;
+  // one piece per thread when dim/8 is a multiple of 128 up to 1024 and the
+  // rows of HC copies fit in registers (4*HC + 1 pieces, or HC + 1 with
+  // partials, under the 128 VGPRs of a 1024-thread workgroup)
+  if constexpr (PARTS || 4 * HC + 1 <= 24) {
+    switch (dim8) {
+      case 128: return launch_exact<HC, 128, PARTS>(g, s);
+      case 256: return launch_exact<HC, 256, PARTS>(g, s);
+      case 384: return launch_exact<HC, 384, PARTS>(g, s);
+      case 512: return launch_exact<HC, 512, PARTS>(g, s);
+      case 640: return launch_exact<HC, 640, PARTS>(g, s);
+      case 768: return launch_exact<HC, 768, PARTS>(g, s);
+      case 896: return launch_exact<HC, 896, PARTS>(g, s);
+      case 1024: return launch_exact<HC, 1024, PARTS>(g, s);
+      default: break;
+    }
+  }
   if (dim8 <= 64) return launch_t<HC, 1, 64, PARTS>(g, s);
   if (dim8 <= 128) return launch_t<HC, 1, 128, PARTS>(g, s);
   const int ch = (dim8 + 255) / 256;

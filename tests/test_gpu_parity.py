@@ -402,8 +402,11 @@ def test_gate_on_shared_kv(name):
 
 
 @pytest.mark.parametrize("hc,dim", [(1, 8), (2, 256), (3, 520), (4, 2048), (4, 7168), (8, 1024), (2, 16384)])
-@pytest.mark.parametrize("T", [1, 2, 15, 65])
+@pytest.mark.parametrize("T", [1, 2, 15, 65, 300])
 def test_gate_shapes(hc, dim, T):
+    """Small T splits the copies over workgroups, T = 300 keeps a token's
+    copies in one; dim/8 in {128, 256, ..., 1024} with few copies takes the
+    one-piece-per-thread kernel, other shapes the general one."""
     E = _E()
     g = torch.Generator(device=DEV).manual_seed(hc * 100003 + dim + T)
     hidden = torch.randn((T, hc, dim), generator=g, device=DEV).to(torch.bfloat16)
@@ -419,6 +422,9 @@ def test_gate_shapes(hc, dim, T):
     assert_close(bf16_values(bits(out)), bf16_values(ref_out), *OUT_TOL, what="out")
     # almost every output is the oracle's bf16 or one step away
     assert np.mean(ulp_distance_bf16(bits(out), ref_out) <= 1) >= 0.999
+    m = mask.cpu().numpy()
+    assert np.array_equal(bits(out)[~m], bits(hidden)[~m])
+    assert np.all(gate_out.cpu().numpy()[~m] == 0)
 
 
 def test_gate_closed_form_and_sign():
@@ -520,6 +526,7 @@ def test_forward_small_hidden_engram_term_dominates():
 
 
 @pytest.mark.parametrize("wfmt,T,dim,hc", [("bf16", 300, 512, 3), ("bf16", 300, 136, 2), ("bf16", 1, 256, 1),
+                                           ("bf16", 300, 1024, 2), ("mxfp8", 257, 1024, 3),
                                            ("mxfp8", 257, 512, 2), ("mxfp8", 200, 160, 2)])
 def test_forward_gate_epilogue_and_plain_paths(wfmt, T, dim, hc):
     """With gate_epilogue and dim % 256 == 0 the forward runs the GEMM's gate
