@@ -32,8 +32,9 @@
 //    publishes stage k+1 sits after the first 4 of the last 16 MFMAs of
 //    stage k, and the next stage's first fragments are read under the other
 //    12.
-//  * MXFP8: a k stage is 128 e4m3 per row (128-byte LDS rows, piece p of row
-//    r at p ^ ((r >> 1) & 7)), two stages.
+//  * MXFP8 (K % 512 == 0, K <= 3584): the bf16 pipeline with 64-e4m3 stages
+//    (gemm_mx_paced_kernel, described above it). Other K: a plain two-stage
+//    kernel with 128-byte k stages (piece p of row r at p ^ ((r >> 1) & 7)).
 //  * Epilogue: the bf16 tile is staged in LDS as [token][n] (512-byte rows,
 //    16-byte chunks XOR-swizzled by token) and written back as whole rows,
 //    16 bytes per lane: 8 full cache lines per store instruction instead of
@@ -464,6 +465,189 @@ void gemm_mxfp8_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict
   store_tile(acc, smem, kv, T, N, t0, n0, wn, wt, lane, wave, ep);
 }
 
+// Paced MXFP8 GEMM: the bf16 kernel's pipeline on the 32x32x64 scaled MFMA.
+// A k stage is 64 e4m3 per row (64-byte LDS rows, the bf16 kernel's layout
+// and swizzle, four stages), i.e. exactly one MFMA k step, and takes the
+// same time as a bf16 stage (16 MFMAs of twice the work), so the DMA pacing
+// (stage k+3 spread over stage k, 8 DMAs per wave) and the barrier position
+// carry over. Lane (row l%32, group g = l/32) reads pieces g and 2+g of its
+// row (k bytes 16g.. and 32+16g..) and passes the E8M0 byte of k block
+// 2*stage + g. All of the tile's scale bytes are staged in LDS once, before
+// the first stage: W's 8 block rows and x's 256 token rows are contiguous in
+// their [rows, K/32] arrays. Per stage: A fragments stream one row block
+// ahead (two register sets); B fragments, A row 0 and the scale bytes of the
+// next stage are read under the last 4 MFMAs, after the barrier.
+constexpr int MX_SCALE_A = LDS_BYTES;           // 8 W block rows x K/32 bytes (<= 1 KiB)
+constexpr int MX_SCALE_B = LDS_BYTES + 1024;    // 256 token rows x K/32 bytes
+constexpr int MX_MAX_KB = (160 * 1024 - MX_SCALE_B) / BN;
+
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_mx_paced_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, int T, int K,
+                          const uint8_t* __restrict__ w, const uint8_t* __restrict__ ws, int N,
+                          uint16_t* __restrict__ kv, int tiles_n, int tiles_t, GateEpi ep) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  int tn, tt;
+  tile_of(blockIdx.x, tiles_n, tiles_t, tn, tt);
+  const int n0 = tn * BM, t0 = tt * BN;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = (wave >> 1) * 128, wt = (wave & 1) * 128;
+  const uint32_t row_bytes = (uint32_t)K;
+  const rsrc_t ra = make_rsrc(w + (int64_t)n0 * K, (uint32_t)min(BM, N - n0) * row_bytes);
+  const rsrc_t rb = make_rsrc(xq + (int64_t)t0 * K, (uint32_t)min(BN, T - t0) * row_bytes);
+  const uint32_t oob = (uint32_t)BM * row_bytes;   // at or past both ranges
+  const int nk = K / 64;
+  const int kb = K / 32;                            // scale bytes per row, a multiple of 16
+
+  // the tile's scale bytes: W block rows n0/32 .. +8 (one DMA, wave 0; lanes
+  // past the range read zeros into the rest of the 1 KiB slot), x rows t0 ..
+  // t0+256 (kb/4 DMAs of 1 KiB over the waves); issued before the stages, so
+  // the prologue's wait covers them
+  {
+    const int nb0 = n0 / 32;
+    const rsrc_t rsa = make_rsrc(ws + (int64_t)nb0 * kb, (uint32_t)(min(8, N / 32 - nb0) * kb));
+    const rsrc_t rsb = make_rsrc(xs + (int64_t)t0 * kb, (uint32_t)(min(BN, T - t0) * kb));
+    if (wave == 0)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(smem + MX_SCALE_A), 16, (uint32_t)lane * 16u,
+                                               0, 0, 0);
+    for (int i = wave; i < kb / 4; i += 4)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)(smem + MX_SCALE_B + i * 1024), 16,
+                                               (uint32_t)(i * 1024 + lane * 16), 0, 0, 0);
+  }
+
+  // DMA i of an operand (i = 0..3): LDS rows 16*(wave + 4i) .. +16, lane l
+  // fetching row 16*(wave+4i) + l/4, piece (l%4) ^ ((row >> 2) & 3).
+  uint32_t doff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (wave + 4 * i) * 16 + (lane >> 2);
+    doff[i] = (uint32_t)r * row_bytes + (uint32_t)(((lane & 3) ^ ((r >> 2) & 3)) * 16);
+  }
+  auto dma = [&](int buf, uint32_t kofs, int j) {
+    const int i = j >> 1, op = j & 1;
+    const uint32_t off = kofs == oob ? oob : doff[i] + kofs;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? rb : ra,
+                                             (lds_ptr_t)(smem + buf * H_STAGE + op * H_TILE +
+                                                         (wave + 4 * i) * 1024),
+                                             16, off, 0, 0, 0);
+  };
+
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  const int lrow = lane & 31, lg = lane >> 5;
+  // LDS reads as vector types: read through the 16-byte struct type, the
+  // compiler could not tell them from the DMAs still writing LDS and waited
+  // for every one of them (vmcnt(0)) before each read
+  auto frag = [&](int buf, int op, int row) {
+    const char* base = smem + buf * H_STAGE + op * H_TILE + row * H_ROW;
+    const int sw = (row >> 2) & 3;
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(base + ((lg ^ sw) << 4));
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(base + (((2 + lg) ^ sw) << 4));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  auto scale_a = [&](int kt, int i) {
+    return (int)(unsigned char)smem[MX_SCALE_A + ((wn >> 5) + i) * kb + kt * 2 + lg];
+  };
+  auto scale_b = [&](int kt, int j) {
+    return (int)(unsigned char)smem[MX_SCALE_B + (wt + j * 32 + lrow) * kb + kt * 2 + lg];
+  };
+
+  i32x8 a0, a1, b[4];
+  int sa[4], sb[4];
+  auto mfma_row = [&](const i32x8& a, int i) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b[j], acc[i][j], 0, 0, 0, sa[i], 0,
+                                                                 sb[j]);
+  };
+
+  // prologue: stages 0 .. H_STAGES-2
+#pragma unroll
+  for (int st = 0; st < H_STAGES - 1; ++st)
+#pragma unroll
+    for (int j = 0; j < H_DMA; ++j) dma(st, st < nk ? (uint32_t)st * H_ROW : oob, j);
+  wait_vm<(H_STAGES - 2) * H_DMA>();
+  bare_barrier();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    b[j] = frag(0, 1, wt + j * 32 + lrow);
+    sa[j] = scale_a(0, j);
+    sb[j] = scale_b(0, j);
+  }
+  a0 = frag(0, 0, wn + lrow);
+
+  int cur = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int nxt = cur + 1 == H_STAGES ? 0 : cur + 1;       // buffer of stage kt+1
+    const int pfb = cur == 0 ? H_STAGES - 1 : cur - 1;       // buffer of stage kt+3 (= kt-1's)
+    const uint32_t kofs = kt + H_STAGES - 1 < nk ? (uint32_t)(kt + H_STAGES - 1) * H_ROW : oob;
+    const int kn = kt + 1 < nk ? kt + 1 : kt;                // scale column of stage kt+1
+    // quarters 0, 1: two DMAs, the next A row block, 4 MFMAs
+    __builtin_amdgcn_sched_barrier(0);
+    dma(pfb, kofs, 0);
+    dma(pfb, kofs, 1);
+    a1 = frag(cur, 0, wn + 32 + lrow);
+    mfma_row(a0, 0);
+    SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1);
+    SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    dma(pfb, kofs, 2);
+    dma(pfb, kofs, 3);
+    a0 = frag(cur, 0, wn + 64 + lrow);
+    mfma_row(a1, 1);
+    SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1);
+    SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1);
+    // quarter 2: the last reads of this stage, then publish stage kt+1: each
+    // wave waits for its own DMAs of that stage (only the 5 issued since may
+    // still fly) and for its LDS reads, then the barrier
+    __builtin_amdgcn_sched_barrier(0);
+    dma(pfb, kofs, 4);
+    a1 = frag(cur, 0, wn + 96 + lrow);
+    mfma_row(a0, 2);
+    SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1);
+    SGB(SG_MFMA, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<(H_STAGES - 3) * H_DMA + 5>();
+    wait_lgkm0();
+    bare_barrier();
+    // quarter 3: stage kt+1's B fragments, A row block 0 and scale bytes
+    // under the last 4 MFMAs
+    __builtin_amdgcn_sched_barrier(0);
+    dma(pfb, kofs, 5);
+    dma(pfb, kofs, 6);
+    dma(pfb, kofs, 7);
+    i32x8 nb[4];
+    int nsa[4], nsb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) nb[j] = frag(nxt, 1, wt + j * 32 + lrow);
+    a0 = frag(nxt, 0, wn + lrow);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      nsa[j] = scale_a(kn, j);
+      nsb[j] = scale_b(kn, j);
+    }
+    mfma_row(a1, 3);
+    SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 5); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 5);
+    SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 4); SGB(SG_MFMA, 1); SGB(SG_DSR, 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      b[j] = nb[j];
+      sa[j] = nsa[j];
+      sb[j] = nsb[j];
+    }
+    cur = nxt;
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  wait_vm<0>();   // the zero-fill DMAs of the last stages land before LDS is reused
+  store_tile(acc, smem, kv, T, N, t0, n0, wn, wt, lane, wave, ep);
+}
+
 hipError_t set_lds(const void* fn) {
   return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
 }
@@ -492,6 +676,16 @@ hipError_t launch_gemm_mxfp8(const uint8_t* xq, const uint8_t* xs, int64_t T, in
                              const uint8_t* ws, int N, void* kv, hipStream_t s, const GateEpi& ep) {
   const int tiles_n = (N + BM - 1) / BM;
   const int tiles_t = (int)((T + BN - 1) / BN);
+  if (K % 512 == 0 && K / 32 <= MX_MAX_KB && N % 32 == 0) {
+    // the paced kernel: 16-byte pieces of scale rows, the tile's scales in LDS
+    const int lds = MX_SCALE_B + BN * (K / 32);
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_mx_paced_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(gemm_mx_paced_kernel, dim3(tiles_n * tiles_t), dim3(THREADS), lds, s, xq, xs,
+                       (int)T, K, w, ws, N, (uint16_t*)kv, tiles_n, tiles_t, ep);
+    return hipGetLastError();
+  }
   hipError_t e = set_lds((const void*)gemm_mxfp8_kernel);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(gemm_mxfp8_kernel, dim3(tiles_n * tiles_t), dim3(THREADS), LDS_BYTES, s, xq, xs,
