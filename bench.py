@@ -189,6 +189,33 @@ def bench_decode(steps, warmup, copies=16):
     return wl, dt, {"wkv": t_wkv, "forward": t_fwd, "single_launch": t_one}
 
 
+def bench_long(steps=5, warmup=2):
+    """The long-prefill workload (T 32768, dim 7168, K 3072, MXFP8 wkv, Zipf
+    ids, 10% masked): event-timed forward and projection (quantize + GEMM),
+    reported beside the headline."""
+    import torch
+
+    from gram_memory_layer_engram_amd import engram as E
+    from gram_memory_layer_engram_amd import workloads as W
+
+    wl = W.WORKLOADS["long"]
+    inp = W.make_inputs(wl, "cuda")
+    stream = torch.cuda.current_stream()
+    out = torch.empty_like(inp["hidden"])
+    plan = E.ForwardPlan(inp["table"], inp["ids"], inp["w"], inp["w_scales"], inp["hidden"], inp["q"],
+                         inp["k"], inp["mask"], wl.eps, wl.clamp, out=out)
+    for _ in range(warmup):
+        plan.run()
+    t_fwd = _events_time(lambda i: plan.run(), steps, stream)
+    x = torch.empty((wl.T, wl.K), dtype=torch.bfloat16, device="cuda")
+    E.lookup(inp["table"], inp["ids"], rows_out=x.view(wl.T, wl.C, wl.head_dim))
+    kv = torch.empty((wl.T, wl.N), dtype=torch.bfloat16, device="cuda")
+    for _ in range(warmup):
+        E.wkv(x, inp["w"], inp["w_scales"], kv=kv)
+    t_wkv = _events_time(lambda i: E.wkv(x, inp["w"], inp["w_scales"], kv=kv), steps, stream)
+    return wl, {"forward": t_fwd, "wkv": t_wkv}
+
+
 def cpu_baseline(budget_s=12.0):
     """The oracle as it stands, on the prefill workload in 512-token blocks,
     passing over the 8192 tokens again until about budget_s seconds of work."""
@@ -310,6 +337,18 @@ def main():
         "wkv_hbm_frac": round((w_bytes + dwl.T * dwl.N * 2) / d_wkv / 1e9 / HBM_PEAK_GBS, 4),
     }
 
+    lwl, lkt = bench_long()
+    l_fwd = statistics.fmean(lkt["forward"]) * 1e-3
+    l_wkv = statistics.fmean(lkt["wkv"]) * 1e-3
+    long = {
+        "workload": "long prefill T=32768, dim 7168, hc 4, K 3072, MXFP8 wkv [35840, 3072], Zipf ids, "
+                    "10% masked",
+        "forward_us_events": round(l_fwd * 1e6, 1),
+        "tokens_per_s": round(lwl.T / l_fwd, 1),
+        "wkv_us": round(l_wkv * 1e6, 1),
+        "wkv_mfma_frac": round(2.0 * lwl.T * lwl.K * lwl.N / l_wkv / 1e12 / FP8_PEAK_TFLOPS, 4),
+    }
+
     cpu = None if a.no_cpu_baseline else cpu_baseline()
     line = {
         "metric": METRIC, "value": round(wl.T / dt, 1), "unit": "tokens/s", "n_gpus": 1,
@@ -319,7 +358,8 @@ def main():
         "config": {"workload": "prefill: T=8192, dim=4096, hc=4, n_hash_cols=16, head_dim=128, "
                                "bf16 tables 33556876 rows (HBM), bf16 wkv [20480, 2048], Zipf(1.1) ids, no mask",
                    "global_batch": wl.T, "parallelism": "none (1 GPU)"},
-        "roofline": roofline, "kernels": kernels, "decode_t16": decode, "cpu_baseline": cpu,
+        "roofline": roofline, "kernels": kernels, "decode_t16": decode, "long_prefill": long,
+        "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
 
