@@ -20,7 +20,10 @@ namespace {
 constexpr int kLookupThreads = 256;
 constexpr int kLookupUnroll = 4;
 
-template <int CPR_T>  // 16-byte pieces per row; 0 = given at run time
+// Idx: the index type of the piece / row arithmetic, 32-bit unless the
+// piece count needs 64 (64-bit division is a branchy routine, and a branch
+// between the id loads makes the compiler wait for each one).
+template <int CPR_T, typename Idx>  // 16-byte pieces per row; 0 = given at run time
 __global__ __launch_bounds__(kLookupThreads) void lookup_kernel(
     const uint4* __restrict__ table, int64_t num_rows,
     const int32_t* __restrict__ ids, int64_t st, int64_t sc, int n_cols,
@@ -31,17 +34,27 @@ __global__ __launch_bounds__(kLookupThreads) void lookup_kernel(
   int bad = 0;
   for (int64_t base = (int64_t)blockIdx.x * kLookupThreads + threadIdx.x;
        base < total; base += stride * kLookupUnroll) {
+    // every id load first, without a branch (a piece past the end reloads the
+    // last piece's id): behind a bounds test the compiler waited for each id
+    // before loading the next, one round trip per piece
+    int32_t idv[kLookupUnroll];
+#pragma unroll
+    for (int u = 0; u < kLookupUnroll; ++u) {
+      const Idx i = (Idx)min(base + u * stride, total - 1);
+      const Idx row = i / (Idx)CPR;
+      const Idx t = row / (Idx)n_cols;
+      const int c = (int)(row - t * (Idx)n_cols);
+      idv[u] = ids[(int64_t)t * st + (int64_t)c * sc];
+    }
     int64_t src[kLookupUnroll];
 #pragma unroll
     for (int u = 0; u < kLookupUnroll; ++u) {
       const int64_t i = base + u * stride;
+      const int64_t row = i / CPR;
+      const int piece = (int)(i - row * CPR);
+      const int64_t id = idv[u];
       src[u] = -1;
       if (i < total) {
-        const int64_t row = i / CPR;
-        const int piece = (int)(i - row * CPR);
-        const int64_t t = row / n_cols;
-        const int c = (int)(row - t * n_cols);
-        const int64_t id = ids[t * st + (int64_t)c * sc];
         if (id >= 0 && id < num_rows) src[u] = id * CPR + piece;
         else bad = 1;
       }
@@ -68,14 +81,20 @@ hipError_t launch_cpr(const void* table, int64_t num_rows, const int32_t* ids,
                        (kLookupThreads * kLookupUnroll);
   const int64_t cap = (int64_t)dev_info().num_cus * 8;
   const int grid = (int)(need < cap ? need : cap);
-  hipLaunchKernelGGL(lookup_kernel<CPR_T>, dim3(grid), dim3(kLookupThreads), 0, s,
-                     (const uint4*)table, num_rows, ids, st, sc, n_cols, cpr,
-                     total, (uint4*)out, err);
+  if (total <= (int64_t)UINT32_MAX)
+    hipLaunchKernelGGL((lookup_kernel<CPR_T, uint32_t>), dim3(grid), dim3(kLookupThreads), 0, s,
+                       (const uint4*)table, num_rows, ids, st, sc, n_cols, cpr,
+                       total, (uint4*)out, err);
+  else
+    hipLaunchKernelGGL((lookup_kernel<CPR_T, uint64_t>), dim3(grid), dim3(kLookupThreads), 0, s,
+                       (const uint4*)table, num_rows, ids, st, sc, n_cols, cpr,
+                       total, (uint4*)out, err);
   return hipGetLastError();
 }
 
 // fp8 rows: grid-stride over 32-element blocks (total = T*C*bpr), two
 // blocks in flight per thread.
+template <typename Idx>   // as in lookup_kernel
 __global__ __launch_bounds__(kLookupThreads) void lookup_fp8_kernel(
     const uint4* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t num_rows, int bpr,
     const int32_t* __restrict__ ids, int64_t st, int64_t sc, int n_cols, int64_t total,
@@ -84,17 +103,24 @@ __global__ __launch_bounds__(kLookupThreads) void lookup_fp8_kernel(
   const int64_t stride = (int64_t)gridDim.x * kLookupThreads;
   int bad = 0;
   for (int64_t base = (int64_t)blockIdx.x * kLookupThreads + threadIdx.x; base < total; base += stride * U) {
+    int32_t idv[U];   // both id loads first, without a branch (as in lookup_kernel)
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const Idx i = (Idx)min(base + u * stride, total - 1);
+      const Idx row = i / (Idx)bpr;
+      const Idx t = row / (Idx)n_cols;
+      const int c = (int)(row - t * (Idx)n_cols);
+      idv[u] = ids[(int64_t)t * st + (int64_t)c * sc];
+    }
     int64_t src[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t i = base + u * stride;
+      const int64_t row = i / bpr;
+      const int part = (int)(i - row * bpr);
+      const int64_t id = idv[u];
       src[u] = -1;
       if (i < total) {
-        const int64_t row = i / bpr;
-        const int part = (int)(i - row * bpr);
-        const int64_t t = row / n_cols;
-        const int c = (int)(row - t * n_cols);
-        const int64_t id = ids[t * st + (int64_t)c * sc];
         if (id >= 0 && id < num_rows) src[u] = id * bpr + part;   // block index in the table
         else bad = 1;
       }
@@ -136,8 +162,12 @@ hipError_t launch_lookup_fp8(const void* codes, const uint8_t* scales, int64_t n
   const int64_t need = (total + kLookupThreads * 2 - 1) / (kLookupThreads * 2);
   const int64_t cap = (int64_t)dev_info().num_cus * 8;
   const int grid = (int)(need < cap ? need : cap);
-  hipLaunchKernelGGL(lookup_fp8_kernel, dim3(grid), dim3(kLookupThreads), 0, s, (const uint4*)codes, scales,
-                     num_rows, bpr, ids, st, sc, n_cols, total, (uint4*)out, err);
+  if (total <= (int64_t)UINT32_MAX)
+    hipLaunchKernelGGL(lookup_fp8_kernel<uint32_t>, dim3(grid), dim3(kLookupThreads), 0, s, (const uint4*)codes,
+                       scales, num_rows, bpr, ids, st, sc, n_cols, total, (uint4*)out, err);
+  else
+    hipLaunchKernelGGL(lookup_fp8_kernel<uint64_t>, dim3(grid), dim3(kLookupThreads), 0, s, (const uint4*)codes,
+                       scales, num_rows, bpr, ids, st, sc, n_cols, total, (uint4*)out, err);
   return hipGetLastError();
 }
 
