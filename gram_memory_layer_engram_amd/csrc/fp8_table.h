@@ -24,18 +24,22 @@ __device__ __forceinline__ float e8m0_to_f32(uint32_t b) {
   return __uint_as_float(b ? (b << 23) : 0x00400000u);
 }
 
-// One 32-element block: codes in 8 words (element 4w+i is byte i of word
-// w), its scale byte -> 16 words of bf16 pairs (element 2i low, 2i+1 high).
-// The e4m3 -> fp32 conversion is gfx950's v_cvt_pk_f32_fp8 (OCP e4m3fn).
+// One word of 4 codes (element i is byte i) under the scale value s -> 2
+// words of bf16 pairs (element 2i low, 2i+1 high). The e4m3 -> fp32
+// conversion is gfx950's v_cvt_pk_f32_fp8 (OCP e4m3fn).
+__device__ __forceinline__ void fp8_word_to_bf16(uint32_t codes, float s, uint32_t* out) {
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes, true);
+  out[0] = pack_bf16x2(lo[0] * s, lo[1] * s);
+  out[1] = pack_bf16x2(hi[0] * s, hi[1] * s);
+}
+
+// One 32-element block: codes in 8 words, its scale byte -> 16 words of
+// bf16 pairs.
 __device__ __forceinline__ void fp8_block_to_bf16(const uint32_t* codes, uint32_t scale_byte, uint32_t* out) {
   const float s = e8m0_to_f32(scale_byte);
 #pragma unroll
-  for (int w = 0; w < 8; ++w) {
-    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes[w], false);
-    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)codes[w], true);
-    out[2 * w] = pack_bf16x2(lo[0] * s, lo[1] * s);
-    out[2 * w + 1] = pack_bf16x2(hi[0] * s, hi[1] * s);
-  }
+  for (int w = 0; w < 8; ++w) fp8_word_to_bf16(codes[w], s, out + 2 * w);
 }
 
 }  // namespace engram

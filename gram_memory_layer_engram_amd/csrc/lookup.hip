@@ -8,8 +8,9 @@
 // row load, then store), and strides over the whole [T*C*pieces] range.
 //
 // fp8 tables (same page, ParallelEngramEmbedding: rows stay fp8 and are
-// dequantized with their ue8m0 per-32 scales on lookup): a thread takes a
-// 32-element block, 32 code bytes + 1 scale byte in, 64 bf16 bytes out.
+// dequantized with their ue8m0 per-32 scales on lookup): a thread takes an
+// 8-element piece, 8 code bytes + its block's scale byte in, 16 bf16 bytes
+// out.
 #include "common.h"
 #include "fp8_table.h"
 
@@ -92,61 +93,62 @@ hipError_t launch_cpr(const void* table, int64_t num_rows, const int32_t* ids,
   return hipGetLastError();
 }
 
-// fp8 rows: grid-stride over 32-element blocks (total = T*C*bpr), two
-// blocks in flight per thread.
+// fp8 rows: grid-stride over 8-element pieces of the output rows (total =
+// T*C*head_dim/8), as lookup_kernel over its 16-byte pieces: a lane reads 8
+// code bytes and its block's scale byte and writes 16 bf16 bytes, so a wave's
+// loads and stores are contiguous runs (a lane per 32-element block wrote
+// 64-byte runs at a 64-byte lane stride, four partial lines per store).
 template <typename Idx>   // as in lookup_kernel
 __global__ __launch_bounds__(kLookupThreads) void lookup_fp8_kernel(
-    const uint4* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t num_rows, int bpr,
+    const uint2* __restrict__ codes, const uint8_t* __restrict__ scales, int64_t num_rows, int cpr,
     const int32_t* __restrict__ ids, int64_t st, int64_t sc, int n_cols, int64_t total,
     uint4* __restrict__ out, int32_t* __restrict__ err) {
-  constexpr int U = 2;
   const int64_t stride = (int64_t)gridDim.x * kLookupThreads;
   int bad = 0;
-  for (int64_t base = (int64_t)blockIdx.x * kLookupThreads + threadIdx.x; base < total; base += stride * U) {
-    int32_t idv[U];   // both id loads first, without a branch (as in lookup_kernel)
+  for (int64_t base = (int64_t)blockIdx.x * kLookupThreads + threadIdx.x; base < total;
+       base += stride * kLookupUnroll) {
+    int32_t idv[kLookupUnroll];   // the id loads first, together
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < kLookupUnroll; ++u) {
       const Idx i = (Idx)min(base + u * stride, total - 1);
-      const Idx row = i / (Idx)bpr;
+      const Idx row = i / (Idx)cpr;
       const Idx t = row / (Idx)n_cols;
       const int c = (int)(row - t * (Idx)n_cols);
       idv[u] = ids[(int64_t)t * st + (int64_t)c * sc];
     }
-    int64_t src[U];
+    int64_t src[kLookupUnroll];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < kLookupUnroll; ++u) {
       const int64_t i = base + u * stride;
-      const int64_t row = i / bpr;
-      const int part = (int)(i - row * bpr);
+      const int64_t row = i / cpr;
+      const int piece = (int)(i - row * cpr);
       const int64_t id = idv[u];
       src[u] = -1;
       if (i < total) {
-        if (id >= 0 && id < num_rows) src[u] = id * bpr + part;   // block index in the table
+        if (id >= 0 && id < num_rows) src[u] = id * cpr + piece;   // 8-code piece of the table
         else bad = 1;
       }
     }
-    uint4 cv[U][2];
-    uint32_t sb[U];
+    uint2 cv[kLookupUnroll];
+    uint32_t sb[kLookupUnroll];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      cv[u][0] = cv[u][1] = make_uint4(0, 0, 0, 0);
-      sb[u] = 127u;
+    for (int u = 0; u < kLookupUnroll; ++u) {
+      cv[u] = make_uint2(0, 0);
+      sb[u] = 127u;                              // a bad id: zero codes, scale 1 -> zero piece
       if (src[u] >= 0) {
-        cv[u][0] = codes[src[u] * 2];
-        cv[u][1] = codes[src[u] * 2 + 1];
-        sb[u] = scales[src[u]];
+        cv[u] = codes[src[u]];
+        sb[u] = scales[src[u] / 4];              // block id * head_dim/32 + piece/4 (cpr = 4 blocks' worth)
       }
     }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
+    for (int u = 0; u < kLookupUnroll; ++u) {
       const int64_t i = base + u * stride;
       if (i >= total) continue;
-      const uint32_t cw[8] = {cv[u][0].x, cv[u][0].y, cv[u][0].z, cv[u][0].w,
-                              cv[u][1].x, cv[u][1].y, cv[u][1].z, cv[u][1].w};
-      uint32_t o[16];
-      fp8_block_to_bf16(cw, sb[u], o);      // a bad id: zero codes, scale 1 -> zero row
-#pragma unroll
-      for (int q = 0; q < 4; ++q) out[i * 4 + q] = make_uint4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
+      const float s = e8m0_to_f32(sb[u]);
+      uint32_t o[4];
+      fp8_word_to_bf16(cv[u].x, s, o);
+      fp8_word_to_bf16(cv[u].y, s, o + 2);
+      out[i] = make_uint4(o[0], o[1], o[2], o[3]);
     }
   }
   if (bad && err) atomicOr(err, 1);
@@ -157,17 +159,17 @@ __global__ __launch_bounds__(kLookupThreads) void lookup_fp8_kernel(
 hipError_t launch_lookup_fp8(const void* codes, const uint8_t* scales, int64_t num_rows, int head_dim,
                              const int32_t* ids, int64_t st, int64_t sc, int64_t T, int n_cols, void* out,
                              int32_t* err, hipStream_t s) {
-  const int bpr = head_dim / 32;
-  const int64_t total = T * n_cols * bpr;
-  const int64_t need = (total + kLookupThreads * 2 - 1) / (kLookupThreads * 2);
+  const int cpr = head_dim / 8;                  // 8-element pieces per row (head_dim % 32 == 0)
+  const int64_t total = T * n_cols * cpr;
+  const int64_t need = (total + kLookupThreads * kLookupUnroll - 1) / (kLookupThreads * kLookupUnroll);
   const int64_t cap = (int64_t)dev_info().num_cus * 8;
   const int grid = (int)(need < cap ? need : cap);
   if (total <= (int64_t)UINT32_MAX)
-    hipLaunchKernelGGL(lookup_fp8_kernel<uint32_t>, dim3(grid), dim3(kLookupThreads), 0, s, (const uint4*)codes,
-                       scales, num_rows, bpr, ids, st, sc, n_cols, total, (uint4*)out, err);
+    hipLaunchKernelGGL(lookup_fp8_kernel<uint32_t>, dim3(grid), dim3(kLookupThreads), 0, s, (const uint2*)codes,
+                       scales, num_rows, cpr, ids, st, sc, n_cols, total, (uint4*)out, err);
   else
-    hipLaunchKernelGGL(lookup_fp8_kernel<uint64_t>, dim3(grid), dim3(kLookupThreads), 0, s, (const uint4*)codes,
-                       scales, num_rows, bpr, ids, st, sc, n_cols, total, (uint4*)out, err);
+    hipLaunchKernelGGL(lookup_fp8_kernel<uint64_t>, dim3(grid), dim3(kLookupThreads), 0, s, (const uint2*)codes,
+                       scales, num_rows, cpr, ids, st, sc, n_cols, total, (uint4*)out, err);
   return hipGetLastError();
 }
 
