@@ -67,6 +67,12 @@ def _events_time(fn, iters, stream):
     return [s.elapsed_time(e) for s, e in zip(starts, ends)]
 
 
+def _pct(v, q):
+    """q-th percentile (0..100) of a list, nearest rank."""
+    v = sorted(v)
+    return v[min(len(v) - 1, max(0, int(round(q / 100.0 * (len(v) - 1)))))]
+
+
 def bench_prefill(steps, warmup):
     import torch
 
@@ -314,7 +320,9 @@ def main():
         "lookup_fp8_table_us": round(avg["lookup_fp8"] * 1e3, 2),
         "lookup_fp8_table_GBs": round(lookup8_bytes / (avg["lookup_fp8"] * 1e-3) / 1e9, 1),
         "wkv_us": round(avg["wkv"] * 1e3, 2), "wkv_us_median": round(med["wkv"] * 1e3, 2),
+        "wkv_us_p10_p90": [round(_pct(kt["wkv"], 10) * 1e3, 2), round(_pct(kt["wkv"], 90) * 1e3, 2)],
         "gate_us": round(avg["gate"] * 1e3, 2),
+        "gate_us_p10_p90": [round(_pct(kt["gate"], 10) * 1e3, 2), round(_pct(kt["gate"], 90) * 1e3, 2)],
         "gate_GBs": round(gate_bytes / (avg["gate"] * 1e-3) / 1e9, 1),
         "forward_us_events": round(avg["forward"] * 1e3, 2),
         "forward_gate_epilogue_us_events": round(avg["forward_gate_epilogue"] * 1e3, 2),
@@ -330,6 +338,9 @@ def main():
         "workload": "decode T=16, dim 4096, MXFP8 wkv [20480, 2048] (40 MiB), 16 weight copies rotated",
         "value": round(dwl.T / ddt, 1), "unit": "tokens/s", "ms_per_step": round(ddt * 1e3, 4),
         "forward_us_events": round(d_fwd * 1e6, 2),
+        "forward_us_median_p10_p90": [round(statistics.median(dkt["forward"]) * 1e3, 2),
+                                      round(_pct(dkt["forward"], 10) * 1e3, 2),
+                                      round(_pct(dkt["forward"], 90) * 1e3, 2)],
         "forward_hbm_frac": round(d_alg / d_fwd / 1e9 / HBM_PEAK_GBS, 4),
         "single_launch_us_events": round(statistics.fmean(dkt["single_launch"]) * 1e3, 2),
         "wkv_us": round(d_wkv * 1e6, 2),
