@@ -11,6 +11,7 @@ import subprocess
 import tempfile
 
 import numpy as np
+import torch
 import pytest
 
 from gram_memory_layer_engram_amd import workloads as W
@@ -171,3 +172,25 @@ def test_generator_values():
     wq, ws = W.make_weight(W.WORKLOADS["decode_t16"].with_T(1))
     assert wq.shape == (20480, 2048) and ws.shape == (640, 64)
     assert int(ws.min()) >= 119 and int(ws.max()) <= 127
+
+
+# ------------------------------------------------------- no fallback path --
+
+
+def test_binding_has_no_cpu_fallback(tmp_path):
+    """Without the built library the binding raises instead of computing
+    anything, and with it, host tensors are refused (every step runs in the
+    HIP kernels)."""
+    from gram_memory_layer_engram_amd import engram
+
+    saved = engram._lib
+    try:
+        engram._lib = None
+        with pytest.raises(RuntimeError, match="not built"):
+            engram.load_library(str(tmp_path / "libengram.so"))
+    finally:
+        engram._lib = saved
+    table = torch.zeros((8, 32), dtype=torch.bfloat16)
+    ids = torch.zeros((2, 3), dtype=torch.int32)
+    with pytest.raises(ValueError, match="device tensors"):
+        engram.lookup(table, ids, rows_out=torch.empty((2, 3, 32), dtype=torch.bfloat16))
