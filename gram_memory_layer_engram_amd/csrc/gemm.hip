@@ -55,6 +55,7 @@ namespace engram {
 namespace {
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int BM = 256;      // W rows per block
@@ -551,11 +552,19 @@ void gemm_mx_paced_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restr
     const i32x4 hi = *reinterpret_cast<const i32x4*>(base + (((2 + lg) ^ sw) << 4));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
-  auto scale_a = [&](int kt, int i) {
-    return (int)(unsigned char)smem[MX_SCALE_A + ((wn >> 5) + i) * kb + kt * 2 + lg];
+  // Scale bytes of 4 stages at a time: for its A row block (or B row) a lane
+  // needs byte 2*stage + lg of the row's K/32; the 8 bytes of stages 4g ..
+  // 4g+3 are one 8-byte LDS read, from which stage 4g+u takes byte 2u + lg.
+  auto scales8 = [&](int kt4, u32x2 (&sa8)[4], u32x2 (&sb8)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sa8[i] = *reinterpret_cast<const u32x2*>(smem + MX_SCALE_A + ((wn >> 5) + i) * kb + kt4 * 2);
+      sb8[i] = *reinterpret_cast<const u32x2*>(smem + MX_SCALE_B + (wt + i * 32 + lrow) * kb + kt4 * 2);
+    }
   };
-  auto scale_b = [&](int kt, int j) {
-    return (int)(unsigned char)smem[MX_SCALE_B + (wt + j * 32 + lrow) * kb + kt * 2 + lg];
+  const uint32_t lsh = (uint32_t)lg * 8u;
+  auto pick = [&](const u32x2& v, int u) {   // u static: byte 2u + lg
+    return (int)(((u < 2 ? v.x : v.y) >> ((uint32_t)(16 * (u & 1)) + lsh)) & 0xffu);
   };
 
   i32x8 a0, a1, b[4];
@@ -574,74 +583,81 @@ void gemm_mx_paced_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restr
     for (int j = 0; j < H_DMA; ++j) dma(st, st < nk ? (uint32_t)st * H_ROW : oob, j);
   wait_vm<(H_STAGES - 2) * H_DMA>();
   bare_barrier();
+  u32x2 sa8[4], sb8[4];
+  scales8(0, sa8, sb8);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    b[j] = frag(0, 1, wt + j * 32 + lrow);
-    sa[j] = scale_a(0, j);
-    sb[j] = scale_b(0, j);
-  }
+  for (int j = 0; j < 4; ++j) b[j] = frag(0, 1, wt + j * 32 + lrow);
   a0 = frag(0, 0, wn + lrow);
 
-  int cur = 0;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int nxt = cur + 1 == H_STAGES ? 0 : cur + 1;       // buffer of stage kt+1
-    const int pfb = cur == 0 ? H_STAGES - 1 : cur - 1;       // buffer of stage kt+3 (= kt-1's)
-    const uint32_t kofs = kt + H_STAGES - 1 < nk ? (uint32_t)(kt + H_STAGES - 1) * H_ROW : oob;
-    const int kn = kt + 1 < nk ? kt + 1 : kt;                // scale column of stage kt+1
-    // quarters 0, 1: two DMAs, the next A row block, 4 MFMAs
-    __builtin_amdgcn_sched_barrier(0);
-    dma(pfb, kofs, 0);
-    dma(pfb, kofs, 1);
-    a1 = frag(cur, 0, wn + 32 + lrow);
-    mfma_row(a0, 0);
-    SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1);
-    SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    dma(pfb, kofs, 2);
-    dma(pfb, kofs, 3);
-    a0 = frag(cur, 0, wn + 64 + lrow);
-    mfma_row(a1, 1);
-    SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1);
-    SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1);
-    // quarter 2: the last reads of this stage, then publish stage kt+1: each
-    // wave waits for its own DMAs of that stage (only the 5 issued since may
-    // still fly) and for its LDS reads, then the barrier
-    __builtin_amdgcn_sched_barrier(0);
-    dma(pfb, kofs, 4);
-    a1 = frag(cur, 0, wn + 96 + lrow);
-    mfma_row(a0, 2);
-    SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1);
-    SGB(SG_MFMA, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vm<(H_STAGES - 3) * H_DMA + 5>();
-    wait_lgkm0();
-    bare_barrier();
-    // quarter 3: stage kt+1's B fragments, A row block 0 and scale bytes
-    // under the last 4 MFMAs
-    __builtin_amdgcn_sched_barrier(0);
-    dma(pfb, kofs, 5);
-    dma(pfb, kofs, 6);
-    dma(pfb, kofs, 7);
-    i32x8 nb[4];
-    int nsa[4], nsb[4];
+  // nk % 4 == 0 (K % 512 == 0): groups of four stages, one per LDS buffer,
+  // so every buffer index below is a constant
+  for (int kt4 = 0; kt4 < nk; kt4 += 4) {
+    u32x2 na8[4], nb8[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) nb[j] = frag(nxt, 1, wt + j * 32 + lrow);
-    a0 = frag(nxt, 0, wn + lrow);
+    for (int u = 0; u < 4; ++u) {
+      const int kt = kt4 + u;
+      const int cur = u, nxt = (u + 1) & 3, pfb = (u + 3) & 3;   // buffers of stages kt, kt+1, kt+3
+      const uint32_t kofs = kt + H_STAGES - 1 < nk ? (uint32_t)(kt + H_STAGES - 1) * H_ROW : oob;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      nsa[j] = scale_a(kn, j);
-      nsb[j] = scale_b(kn, j);
+      for (int i = 0; i < 4; ++i) {
+        sa[i] = pick(sa8[i], u);
+        sb[i] = pick(sb8[i], u);
+      }
+      // quarters 0, 1: two DMAs, the next A row block, 4 MFMAs
+      __builtin_amdgcn_sched_barrier(0);
+      dma(pfb, kofs, 0);
+      dma(pfb, kofs, 1);
+      a1 = frag(cur, 0, wn + 32 + lrow);
+      mfma_row(a0, 0);
+      SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1);
+      SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      dma(pfb, kofs, 2);
+      dma(pfb, kofs, 3);
+      a0 = frag(cur, 0, wn + 64 + lrow);
+      mfma_row(a1, 1);
+      SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1);
+      SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1);
+      // quarter 2: the last reads of this stage, then publish stage kt+1: each
+      // wave waits for its own DMAs of that stage (only the 5 issued since may
+      // still fly) and for its LDS reads, then the barrier
+      __builtin_amdgcn_sched_barrier(0);
+      dma(pfb, kofs, 4);
+      a1 = frag(cur, 0, wn + 96 + lrow);
+      mfma_row(a0, 2);
+      SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1);
+      SGB(SG_MFMA, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vm<(H_STAGES - 3) * H_DMA + 5>();
+      wait_lgkm0();
+      bare_barrier();
+      // quarter 3: stage kt+1's B fragments and A row block 0 (and, closing a
+      // group, the next group's scale bytes) under the last 4 MFMAs
+      __builtin_amdgcn_sched_barrier(0);
+      dma(pfb, kofs, 5);
+      dma(pfb, kofs, 6);
+      dma(pfb, kofs, 7);
+      i32x8 nb[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) nb[j] = frag(nxt, 1, wt + j * 32 + lrow);
+      a0 = frag(nxt, 0, wn + lrow);
+      if (u == 3) scales8(min(kt4 + 4, nk - 4), na8, nb8);   // the last group reloads itself, unused
+      mfma_row(a1, 3);
+      if (u == 3) {
+        SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 5); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1);
+        SGB(SG_DSR, 5); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 4); SGB(SG_MFMA, 1); SGB(SG_DSR, 4);
+      } else {
+        SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 4); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1);
+        SGB(SG_DSR, 3); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 3); SGB(SG_MFMA, 1);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = nb[j];
     }
-    mfma_row(a1, 3);
-    SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 5); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 5);
-    SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 4); SGB(SG_MFMA, 1); SGB(SG_DSR, 4);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      b[j] = nb[j];
-      sa[j] = nsa[j];
-      sb[j] = nsb[j];
+    for (int i = 0; i < 4; ++i) {
+      sa8[i] = na8[i];
+      sb8[i] = nb8[i];
     }
-    cur = nxt;
   }
   __builtin_amdgcn_sched_barrier(0);
   wait_vm<0>();   // the zero-fill DMAs of the last stages land before LDS is reused
