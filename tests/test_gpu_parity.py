@@ -481,6 +481,34 @@ def test_forward(name):
     assert np.max(np.abs(g - ref["gate"])) <= 2e-2
 
 
+@pytest.mark.parametrize("name", ["mid", "prefill", "long"])
+def test_forward_gate_epilogue_full_size(name):
+    """The gate-epilogue forward at the workloads' full sizes, in the launch
+    configuration bench.py times: sampled tokens against the oracle, masked
+    rows copied, and the same bf16 keys as the default forward (gates within
+    the reordering of their fp32 sums)."""
+    E = _E()
+    inp = inputs(name)
+    wl = inp["wl"]
+    _say(f"forward gate epilogue {name} T={wl.T}")
+    args = (inp["table"], inp["ids"], inp["w"], inp["w_scales"], inp["hidden"], inp["q"], inp["k"],
+            inp["mask"], wl.eps, wl.clamp)
+    g_epi = torch.empty((wl.T, wl.hc), dtype=torch.float32, device=DEV)
+    g_def = torch.empty((wl.T, wl.hc), dtype=torch.float32, device=DEV)
+    out = E.forward(*args, gate_out=g_epi, gate_epilogue=True).clone()
+    E.forward(*args, gate_out=g_def)
+    torch.cuda.synchronize()
+    toks = sample_tokens(wl.T, SAMPLE, seed=5)
+    ref = oracle_forward_sample(inp, toks)
+    got = bits(out)[toks]
+    assert_close(bf16_values(got), bf16_values(ref["out"]), *OUT_TOL, what="out")
+    if inp["mask"] is not None:
+        full_m = inp["mask"].cpu().numpy()
+        assert np.array_equal(bits(out)[~full_m], bits(inp["hidden"])[~full_m])
+    assert np.max(np.abs(g_epi.cpu().numpy()[toks] - ref["gate"])) <= 2e-2
+    assert np.max(np.abs(g_epi.cpu().numpy() - g_def.cpu().numpy())) <= GATE_ABS
+
+
 def test_forward_mask_none_equals_all_true_and_empty():
     E = _E()
     inp = inputs("tiny")
