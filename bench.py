@@ -275,7 +275,7 @@ def main():
     a = ap.parse_args()
     if a.gpus != 1:
         print("bench.py measures one GPU: the Engram hot path here has no multi-GPU mode "
-              "(every token is independent; see DESIGN.md for how it would shard).", file=sys.stderr)
+              "(every token is independent, so it would shard by tokens with no exchange).", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -40,7 +40,7 @@ extern "C" {
 enum {
   ENGRAM_OK = 0,
   ENGRAM_EINVAL = 1,       /* NULL required pointer, bad size, misalignment */
-  ENGRAM_EUNSUPPORTED = 2, /* a valid shape this build has no kernel for */
+  ENGRAM_EUNSUPPORTED = 2, /* a valid shape the library has no kernel for */
   ENGRAM_EHIP = 3          /* a HIP runtime error at launch */
 };
 
