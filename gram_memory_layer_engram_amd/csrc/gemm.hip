@@ -224,10 +224,11 @@ __device__ __forceinline__ void store_tile(f32x16 (&acc)[4][4], char* smem, uint
     hid[it] = make_uint4(0, 0, 0, 0);
     if (t0 + t < T) hid[it] = *reinterpret_cast<const uint4*>(ep.hidden + ((int64_t)(t0 + t) * ep.hc + h) * ep.dim + d);
   }
+  // per-lane sums of this lane's 8 columns, one pair per row (iteration it)
+  float dts[32], kss[32];
 #pragma unroll
   for (int it = 0; it < 32; ++it) {
     const int t = wave * 64 + it * 2 + (lane >> 5);
-    const bool live = t0 + t < T;
     const uint4 kv8 = lds_row(t);
     const uint4 h8 = hid[it];
     const uint32_t kw[4] = {kv8.x, kv8.y, kv8.z, kv8.w}, hw[4] = {h8.x, h8.y, h8.z, h8.w};
@@ -240,14 +241,26 @@ __device__ __forceinline__ void store_tile(f32x16 (&acc)[4][4], char* smem, uint
       dt = fmaf(bf16lo(hw[e]) * qk[2 * e], k0, dt);
       dt = fmaf(bf16hi(hw[e]) * qk[2 * e + 1], k1, dt);
     }
-    // the 32 lanes of a row, in a fixed order
-#pragma unroll
-    for (int off = 16; off >= 1; off >>= 1) {
-      dt += __shfl_xor(dt, off, 64);
-      ks += __shfl_xor(ks, off, 64);
-    }
-    if (c == 0 && live) ep.part[((int64_t)h * T + t0 + t) * tiles + tile] = make_float2(dt, ks);
+    dts[it] = dt;
+    kss[it] = ks;
   }
+  // Sum over the 32 lanes of each half-wave for all 32 rows at once: at
+  // each step lane c keeps the half of its rows selected by bit w of c and
+  // adds the partner's (lane c^w) copy of them, so 31 exchanges per sum
+  // instead of 5 per row; lane c ends with row it = c, in a fixed order.
+#pragma unroll
+  for (int w = 16; w >= 1; w >>= 1) {
+    const bool upper = (c & w) != 0;
+#pragma unroll
+    for (int i = 0; i < w; ++i) {
+      const float rd = __shfl_xor(upper ? dts[i] : dts[i + w], w, 64);
+      const float rk = __shfl_xor(upper ? kss[i] : kss[i + w], w, 64);
+      dts[i] = (upper ? dts[i + w] : dts[i]) + rd;
+      kss[i] = (upper ? kss[i + w] : kss[i]) + rk;
+    }
+  }
+  const int t = wave * 64 + c * 2 + (lane >> 5);
+  if (t0 + t < T) ep.part[((int64_t)h * T + t0 + t) * tiles + tile] = make_float2(dts[0], kss[0]);
 }
 
 // bf16 wkv GEMM (see the file comment). KTAIL: K % 32 != 0, the last stage's
