@@ -9,8 +9,10 @@ synthetic and already resident in HBM when the timed region starts.
 Prints one JSON line. ``value`` is prefill tokens/s; ``decode_t16`` carries
 the decode workload (T = 16, MXFP8 wkv) measured cold: 16 copies of the
 weight are rotated so no step finds it in the 256 MB Infinity Cache.
-``roofline`` is the dominant kernel (the wkv GEMM, MFMA-bound) with its
-duration taken from HIP events on the launch stream inside the timed region.
+``roofline`` is the dominant kernel (the wkv GEMM with the gate epilogue that
+the default forward launches, MFMA-bound) with its duration taken from HIP
+events on the launch stream, around calls of engram_wkv_gate_partials in the
+same launch configuration, made just before the timed steps.
 ``cpu_baseline`` is the CPU oracle on a bounded sample of the same workload.
 """
 
@@ -87,21 +89,21 @@ def bench_prefill(steps, warmup):
                           inp["k"], None, wl.eps, wl.clamp, out)
     ws = torch.empty(E.forward_workspace_size(args), dtype=torch.uint8, device="cuda")
 
-    def fwd(_=0, gate_epilogue=False):
+    def fwd(_=0, store_kv=False):
         E.forward(inp["table"], inp["ids"], inp["w"], None, inp["hidden"], inp["q"], inp["k"],
-                  None, wl.eps, wl.clamp, out=out, workspace=ws, gate_epilogue=gate_epilogue)
+                  None, wl.eps, wl.clamp, out=out, workspace=ws, store_kv=store_kv)
 
     for _ in range(warmup):
         fwd()
 
     # Per-kernel durations, before the timed steps so that those start from
-    # the clocks and caches of a running loop: the default forward and the
-    # one with the GEMM's gate epilogue (keys never stored), alternated call
-    # by call so both see the same clocks; then the three steps
-    # engram_forward enqueues, called one by one. All event-timed on the
-    # launch stream.
+    # the clocks and caches of a running loop: the default forward (the
+    # GEMM's gate epilogue, keys never stored) and the store-kv forward
+    # (kv stored, plain gate), alternated call by call so both see the same
+    # clocks; then the steps of each route called one by one through
+    # pre-marshalled C calls. All event-timed on the launch stream.
     t_both = _events_time(lambda i: fwd(i, i % 2 == 1), 2 * steps, stream)
-    t_fwd, t_fwd_epi = t_both[0::2], t_both[1::2]
+    t_fwd, t_fwd_kv = t_both[0::2], t_both[1::2]
     rows = torch.empty((wl.T, wl.C, wl.head_dim), dtype=torch.bfloat16, device="cuda")
     kv = torch.empty((wl.T, wl.N), dtype=torch.bfloat16, device="cuda")
     x = rows.view(wl.T, wl.K)
@@ -111,6 +113,14 @@ def bench_prefill(steps, warmup):
     look = (inp["table"].data_ptr(), inp["table"].shape[0], wl.head_dim, ids.data_ptr(), ids.stride(0),
             ids.stride(1), wl.T, wl.C, rows.data_ptr(), None, sp)
     t_lookup = _events_time(lambda i: L.engram_lookup(*look), steps, stream)
+    value = torch.empty((wl.T, wl.dim), dtype=torch.bfloat16, device="cuda")
+    parts = torch.empty((wl.hc, wl.T, wl.dim // 256, 2), dtype=torch.float32, device="cuda")
+    fused = (x.data_ptr(), wl.T, wl.K, inp["w"].data_ptr(), None, E.W_BF16, wl.hc, wl.dim,
+             inp["hidden"].data_ptr(), inp["q"].data_ptr(), inp["k"].data_ptr(), value.data_ptr(),
+             parts.data_ptr(), None, 0, sp)
+    if L.engram_wkv_gate_partials(*fused) != 0:
+        raise RuntimeError("engram_wkv_gate_partials refused the prefill shapes")
+    t_fused = _events_time(lambda i: L.engram_wkv_gate_partials(*fused), steps, stream)
     t_wkv = _events_time(lambda i: E.wkv(x, inp["w"], kv=kv), steps, stream)
     t_gate = _events_time(lambda i: E.gate(inp["hidden"], kv, inp["q"], inp["k"], None, wl.eps,
                                            wl.clamp, out=out), steps, stream)
@@ -133,8 +143,8 @@ def bench_prefill(steps, warmup):
     for _ in range(warmup):
         L.engram_lookup_fp8(*look8)
     t_lookup8 = _events_time(lambda i: L.engram_lookup_fp8(*look8), steps, stream)
-    return wl, dt, {"lookup": t_lookup, "wkv": t_wkv, "gate": t_gate, "lookup_fp8": t_lookup8,
-                    "forward": t_fwd, "forward_gate_epilogue": t_fwd_epi}
+    return wl, dt, {"lookup": t_lookup, "wkv_gate_partials": t_fused, "wkv": t_wkv, "gate": t_gate,
+                    "lookup_fp8": t_lookup8, "forward": t_fwd, "forward_store_kv": t_fwd_kv}
 
 
 def bench_decode(steps, warmup, copies=16):
@@ -301,14 +311,15 @@ def main():
     med = {k: statistics.median(v) for k, v in kt.items()}
     avg = {k: statistics.fmean(v) for k, v in kt.items()}
     flops = 2.0 * wl.T * wl.K * wl.N
-    wkv_s = avg["wkv"] * 1e-3
-    achieved = flops / wkv_s / 1e12
+    fused_s = avg["wkv_gate_partials"] * 1e-3
+    achieved = flops / fused_s / 1e12
     roofline = {
-        "kernel": "gemm_bf16_kernel (wkv projection, 8192 x 20480 x 2048)",
+        "kernel": "gemm_bf16_kernel with the gate epilogue (engram_wkv_gate_partials, the default "
+                  "forward's projection: 8192 x 20480 x 2048)",
         "bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
         "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-        "traffic": _traffic("gemm_bf16_kernel", "gram_memory_layer_engram_amd/csrc/gemm.hip"),
-        "traffic_unit": "bytes per launch past L2 (rocprofv3 FETCH_SIZE x2.0 + WRITE_SIZE, copy-calibrated)",
+        "traffic": _traffic("gemm_bf16_kernel_gate_epilogue", "gram_memory_layer_engram_amd/csrc/gemm.hip"),
+        "traffic_unit": "bytes per launch past L2 (rocprofv3 FETCH_SIZE + WRITE_SIZE, each copy-calibrated)",
     }
     # the HBM-bound kernels of the same step, against 8 TB/s
     lookup_bytes = wl.T * wl.C * (4 + 2 * 2 * wl.head_dim)
@@ -319,13 +330,17 @@ def main():
         "lookup_GBs": round(lookup_bytes / (avg["lookup"] * 1e-3) / 1e9, 1),
         "lookup_fp8_table_us": round(avg["lookup_fp8"] * 1e3, 2),
         "lookup_fp8_table_GBs": round(lookup8_bytes / (avg["lookup_fp8"] * 1e-3) / 1e9, 1),
+        "wkv_gate_partials_us": round(avg["wkv_gate_partials"] * 1e3, 2),
+        "wkv_gate_partials_us_p10_p90": [round(_pct(kt["wkv_gate_partials"], 10) * 1e3, 2),
+                                         round(_pct(kt["wkv_gate_partials"], 90) * 1e3, 2)],
         "wkv_us": round(avg["wkv"] * 1e3, 2), "wkv_us_median": round(med["wkv"] * 1e3, 2),
         "wkv_us_p10_p90": [round(_pct(kt["wkv"], 10) * 1e3, 2), round(_pct(kt["wkv"], 90) * 1e3, 2)],
+        "wkv_mfma_frac": round(flops / (avg["wkv"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
         "gate_us": round(avg["gate"] * 1e3, 2),
         "gate_us_p10_p90": [round(_pct(kt["gate"], 10) * 1e3, 2), round(_pct(kt["gate"], 90) * 1e3, 2)],
         "gate_GBs": round(gate_bytes / (avg["gate"] * 1e-3) / 1e9, 1),
         "forward_us_events": round(avg["forward"] * 1e3, 2),
-        "forward_gate_epilogue_us_events": round(avg["forward_gate_epilogue"] * 1e3, 2),
+        "forward_store_kv_us_events": round(avg["forward_store_kv"] * 1e3, 2),
     }
 
     dwl, ddt, dkt = bench_decode(max(a.steps, 100), a.warmup)

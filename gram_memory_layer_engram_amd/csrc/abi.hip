@@ -86,6 +86,18 @@ int run_wkv(const void* x, int64_t T, int32_t K, const void* w,
   return hip_status(run_mx_projection(xq, xs, T, K, w, w_scales, N, kv, s, ep));
 }
 
+// MXFP8 quantize + tiled scaled-MFMA GEMM whatever T is (the gate epilogue
+// lives in the tiled GEMM only).
+int run_wkv_tiled(const void* x, int64_t T, int32_t K, const void* w, const uint8_t* w_scales,
+                  int32_t w_format, int32_t N, void* kv, void* workspace, hipStream_t s, const GateEpi& ep) {
+  if (T == 0) return ENGRAM_OK;
+  if (w_format == ENGRAM_W_BF16) return hip_status(launch_gemm_bf16(x, T, K, w, N, kv, s, ep));
+  uint8_t* xq = (uint8_t*)workspace;
+  uint8_t* xs = xq + round_up((size_t)T * K);
+  if (launch_mx_quantize(x, T, K, xq, xs, s) != hipSuccess) return ENGRAM_EHIP;
+  return hip_status(launch_gemm_mxfp8(xq, xs, T, K, (const uint8_t*)w, w_scales, N, kv, s, ep));
+}
+
 int check_gate(const void* hidden, const void* kv, const void* q, const void* k,
                int64_t T, int32_t hc, int32_t dim, void* out) {
   if (T < 0 || hc <= 0 || dim <= 0) return ENGRAM_EINVAL;
@@ -177,6 +189,30 @@ size_t engram_wkv_workspace_size(int64_t T, int32_t K, int32_t N,
   return w_format == ENGRAM_W_MXFP8 ? mx_stage_bytes(T, K) : 0;
 }
 
+int engram_wkv_gate_partials(const void* x, int64_t T, int32_t K, const void* w,
+                             const uint8_t* w_scales, int32_t w_format, int32_t hc,
+                             int32_t dim, const void* hidden, const void* q_weight,
+                             const void* k_weight, void* value, float* partials,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  if (hc <= 0 || dim <= 0) return ENGRAM_EINVAL;
+  if (hc > 8 || dim % 256 != 0) return ENGRAM_EUNSUPPORTED;
+  const int64_t N64 = (int64_t)(hc + 1) * dim;
+  if (N64 > INT32_MAX) return ENGRAM_EUNSUPPORTED;
+  const int32_t N = (int32_t)N64;
+  int st = check_wkv(x, T, K, w, w_scales, w_format, N, value);
+  if (st != ENGRAM_OK) return st;
+  st = check_gate(hidden, value, q_weight, k_weight, T, hc, dim, value);
+  if (st != ENGRAM_OK) return st;
+  if (T == 0) return ENGRAM_OK;
+  if (!partials || ((uintptr_t)partials & 7u)) return ENGRAM_EINVAL;
+  const size_t need = engram_wkv_workspace_size(T, K, N, w_format);
+  if (workspace_bytes < need || (need && (!workspace || ((uintptr_t)workspace % kAlign))))
+    return ENGRAM_EINVAL;
+  const GateEpi ep{(const uint16_t*)hidden, (const uint16_t*)q_weight, (const uint16_t*)k_weight,
+                   (uint16_t*)value, (float2*)partials, hc, dim};
+  return run_wkv_tiled(x, T, K, w, w_scales, w_format, N, value, workspace, (hipStream_t)stream, ep);
+}
+
 int engram_wkv(const void* x, int64_t T, int32_t K, const void* w,
                const uint8_t* w_scales, int32_t w_format, int32_t N, void* kv,
                void* workspace, size_t workspace_bytes, void* stream) {
@@ -223,7 +259,7 @@ size_t engram_forward_workspace_size(const engram_forward_args* a) {
 // Shared argument checks of the two forward entry points; sets K and N.
 int check_forward(const engram_forward_args* a, void* workspace, size_t workspace_bytes, int32_t* K,
                   int32_t* N) {
-  if (!a || (a->options & ~ENGRAM_FORWARD_GATE_EPILOGUE)) return ENGRAM_EINVAL;
+  if (!a || (a->options & ~ENGRAM_FORWARD_STORE_KV)) return ENGRAM_EINVAL;
   const int64_t K64 = (int64_t)a->n_cols * a->head_dim;
   const int64_t N64 = (int64_t)(a->hc + 1) * a->dim;
   if (K64 > INT32_MAX || N64 > INT32_MAX) return ENGRAM_EUNSUPPORTED;
@@ -256,13 +292,13 @@ int engram_forward(const engram_forward_args* a, void* workspace,
   void* rows = ws;
   void* kv = ws + round_up((size_t)a->T * K * 2);
   void* mx = (uint8_t*)kv + round_up((size_t)a->T * N * 2);
-  // With ENGRAM_FORWARD_GATE_EPILOGUE, when a tiled GEMM runs and a
+  // Unless ENGRAM_FORWARD_STORE_KV is set, when a tiled GEMM runs and a
   // 256-column tile lies inside one key block (dim % 256 == 0), its epilogue
   // turns key tiles into the gate's partial sums and stores only the value:
   // kv's keys never reach HBM. The value and partials take kv's place in the
   // workspace.
   const bool tiled = a->w_format == ENGRAM_W_BF16 || !gemv_mxfp8_supported(a->T, K);
-  const bool epi = (a->options & ENGRAM_FORWARD_GATE_EPILOGUE) && tiled && a->dim % 256 == 0;
+  const bool epi = !(a->options & ENGRAM_FORWARD_STORE_KV) && tiled && a->dim % 256 == 0;
   uint16_t* value = (uint16_t*)kv;
   float2* part = (float2*)((uint8_t*)kv + round_up((size_t)a->T * a->dim * 2));
   const GateEpi ep = epi ? GateEpi{(const uint16_t*)a->hidden, (const uint16_t*)a->q_weight,

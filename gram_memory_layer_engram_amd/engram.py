@@ -18,7 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libengram.so")
 
 ENGRAM_OK, ENGRAM_EINVAL, ENGRAM_EUNSUPPORTED, ENGRAM_EHIP = 0, 1, 2, 3
 W_BF16, W_MXFP8 = 0, 1
-FORWARD_GATE_EPILOGUE = 1
+FORWARD_STORE_KV = 1
 
 _vp = ctypes.c_void_p
 _i32 = ctypes.c_int32
@@ -50,6 +50,8 @@ EXPORTS = {
     "engram_mx_quantize": (_i32, [_vp, _i64, _i32, _vp, _vp, _vp]),
     "engram_wkv_workspace_size": (_sz, [_i64, _i32, _i32, _i32]),
     "engram_wkv": (_i32, [_vp, _i64, _i32, _vp, _vp, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "engram_wkv_gate_partials": (_i32, [_vp, _i64, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
+                                        _vp, _sz, _vp]),
     "engram_gate": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _f32, _f32, _vp, _vp, _vp]),
     "engram_forward_workspace_size": (_sz, [ctypes.POINTER(ForwardArgs)]),
     "engram_forward": (_i32, [ctypes.POINTER(ForwardArgs), _vp, _sz, _vp]),
@@ -187,6 +189,44 @@ def wkv(x: torch.Tensor, w: torch.Tensor, w_scales: torch.Tensor | None = None,
     return kv
 
 
+def wkv_gate_partials(x: torch.Tensor, w: torch.Tensor, w_scales: torch.Tensor | None,
+                      hidden: torch.Tensor, q_weight: torch.Tensor, k_weight: torch.Tensor,
+                      value: torch.Tensor | None = None, partials: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None):
+    """The projection fused with the gate's kv-side sums: returns (value
+    [T, dim] bf16, partials [hc, T, dim/256, 2] fp32 = (sum hidden*q*k*key,
+    sum key^2) per 256-column key tile). MXFP8 when ``w_scales`` is given."""
+    L = load_library()
+    for t, n in ((x, "x"), (w, "w"), (hidden, "hidden"), (q_weight, "q_weight"), (k_weight, "k_weight")):
+        _dense(t, n)
+    T, K = x.shape
+    _, hc, dim = hidden.shape
+    N = (hc + 1) * dim
+    fmt = W_BF16 if w_scales is None else W_MXFP8
+    if tuple(w.shape) != (N, K):
+        raise ValueError(f"w must be [{N}, {K}], got {tuple(w.shape)}")
+    if fmt == W_MXFP8:
+        _dense(w_scales, "w_scales")
+    if value is None:
+        value = torch.empty((T, dim), dtype=torch.bfloat16, device=x.device)
+    if partials is None:
+        partials = torch.empty((hc, T, max(1, dim // 256), 2), dtype=torch.float32, device=x.device)
+    if tuple(value.shape) != (T, dim) or value.dtype != torch.bfloat16:
+        raise ValueError(f"value must be bf16 [{T}, {dim}]")
+    if tuple(partials.shape) != (hc, T, max(1, dim // 256), 2) or partials.dtype != torch.float32:
+        raise ValueError(f"partials must be fp32 [{hc}, {T}, {dim // 256}, 2]")
+    _dense(value, "value")
+    _dense(partials, "partials")
+    need = L.engram_wkv_workspace_size(T, K, N, fmt)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel()
+    _check(L.engram_wkv_gate_partials(_ptr(x), T, K, _ptr(w), _ptr(w_scales), fmt, hc, dim, _ptr(hidden),
+                                      _ptr(q_weight), _ptr(k_weight), _ptr(value), _ptr(partials),
+                                      _ptr(workspace), ws_bytes, _stream()))
+    return value, partials
+
+
 def gate(hidden: torch.Tensor, kv: torch.Tensor, q_weight: torch.Tensor, k_weight: torch.Tensor,
          token_mask: torch.Tensor | None = None, eps: float = 1e-6, clamp: float = 1e-6,
          out: torch.Tensor | None = None, gate_out: torch.Tensor | None = None) -> torch.Tensor:
@@ -205,7 +245,7 @@ def gate(hidden: torch.Tensor, kv: torch.Tensor, q_weight: torch.Tensor, k_weigh
 
 def forward_args(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask,
                  eps, clamp, out, gate_out=None, err_flag=None, table_scales=None,
-                 gate_epilogue=False) -> ForwardArgs:
+                 store_kv=False) -> ForwardArgs:
     T, hc, dim = hidden.shape
     a = ForwardArgs()
     a.table = _ptr(table); a.num_rows = table.shape[0]
@@ -224,7 +264,7 @@ def forward_args(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token
         if table.dtype != torch.uint8 or tuple(table_scales.shape) != (table.shape[0], table.shape[1] // 32):
             raise ValueError("fp8 table: uint8 codes [rows, hd] and scales [rows, hd / 32]")
     a.table_scales = _ptr(table_scales)
-    a.options = FORWARD_GATE_EPILOGUE if gate_epilogue else 0
+    a.options = FORWARD_STORE_KV if store_kv else 0
     return a
 
 
@@ -234,12 +274,13 @@ def forward_workspace_size(args: ForwardArgs) -> int:
 
 def forward(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask=None,
             eps=1e-6, clamp=1e-6, out=None, gate_out=None, err_flag=None, workspace=None,
-            single_launch=False, table_scales=None, gate_epilogue=False):
+            single_launch=False, table_scales=None, store_kv=False):
     """One Engram layer forward: lookup -> (MXFP8 quantize) -> wkv -> gate.
     ``single_launch`` selects engram_forward_single_launch (decode shapes);
     ``table_scales`` makes ``table`` an fp8 table (uint8 e4m3 codes);
-    ``gate_epilogue`` sets ENGRAM_FORWARD_GATE_EPILOGUE (the tiled GEMM
-    reduces key tiles to the gate's partial sums, keys never stored)."""
+    ``store_kv`` sets ENGRAM_FORWARD_STORE_KV: kv is stored whole and the
+    plain gate reads it, instead of the default where the tiled GEMM reduces
+    key tiles to the gate's partial sums and stores only the value."""
     L = load_library()
     for t, n in ((table, "table"), (w, "w"), (hidden, "hidden"),
                  (q_weight, "q_weight"), (k_weight, "k_weight")):
@@ -247,7 +288,7 @@ def forward(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask
     if out is None:
         out = torch.empty_like(hidden)
     args = forward_args(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask,
-                        eps, clamp, out, gate_out, err_flag, table_scales, gate_epilogue)
+                        eps, clamp, out, gate_out, err_flag, table_scales, store_kv)
     need = L.engram_forward_workspace_size(ctypes.byref(args))
     if workspace is None and need:
         workspace = new_forward_workspace(need, hidden.device)
@@ -271,7 +312,7 @@ class ForwardPlan:
 
     def __init__(self, table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask=None,
                  eps=1e-6, clamp=1e-6, out=None, gate_out=None, err_flag=None, workspace=None,
-                 stream=None, single_launch=False, table_scales=None, gate_epilogue=False):
+                 stream=None, single_launch=False, table_scales=None, store_kv=False):
         L = load_library()
         for t, n in ((table, "table"), (w, "w"), (hidden, "hidden"),
                      (q_weight, "q_weight"), (k_weight, "k_weight")):
@@ -282,7 +323,7 @@ class ForwardPlan:
         self._keep = (table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask, gate_out,
                       err_flag, table_scales)
         self.args = forward_args(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask,
-                                 eps, clamp, out, gate_out, err_flag, table_scales, gate_epilogue)
+                                 eps, clamp, out, gate_out, err_flag, table_scales, store_kv)
         need = L.engram_forward_workspace_size(ctypes.byref(self.args))
         if workspace is None and need:
             workspace = new_forward_workspace(need, hidden.device)

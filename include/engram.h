@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define ENGRAM_ABI_VERSION 3
+#define ENGRAM_ABI_VERSION 4
 
 /* Status codes. */
 enum {
@@ -141,6 +141,38 @@ int engram_wkv(const void* x, int64_t T, int32_t K, const void* w,
                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * engram_wkv_gate_partials -- the projection fused with the gate's kv-side
+ *   sums: [P-rocm] _engram_gate_partials_kernel / _engram_gate_finish_kernel
+ *   split the gate into per-shard partial sums and a finish step; here a
+ *   shard is a 256-column tile of the projection. kv = bf16(x . W^T) is
+ *   computed by the tiled GEMM engram_wkv runs (bit for bit the same where
+ *   engram_wkv runs that GEMM), but only the
+ *   value block is stored; each key tile (copy h, columns 256i .. 256i+255)
+ *   is reduced, per token t, against hidden, q and k:
+ *     partials[2*((h*T + t)*(dim/256) + i)]     = sum hidden*q*k*key
+ *     partials[2*((h*T + t)*(dim/256) + i) + 1] = sum key^2
+ *   over the tile, on the bf16-rounded keys (fp32, fixed order). The keys
+ *   never reach memory. engram_forward uses it where it applies and finishes
+ *   the gate from the partials.
+ *
+ *   x, T, K, w, w_scales, w_format: as engram_wkv, with N = (hc+1)*dim.
+ *   hidden      bf16 [T, hc, dim];  q_weight, k_weight  bf16 [hc, dim]
+ *   value       bf16 [T, dim] (kv's value block)
+ *   partials    fp32 [hc, T, dim/256, 2], 8-byte aligned
+ *   workspace   engram_wkv_workspace_size(T, K, (hc+1)*dim, w_format) bytes
+ *   Errors: ENGRAM_EINVAL for hc or dim <= 0, a NULL or misaligned pointer,
+ *   or a short workspace; T = 0 is a no-op. Asynchronous on `stream`.
+ *   Shapes: as engram_wkv, plus dim % 256 == 0 and 1 <= hc <= 8; other
+ *   shapes return ENGRAM_EUNSUPPORTED. MXFP8 always runs the tiled GEMM
+ *   here (engram_wkv would take the decode GEMV for T <= 64).
+ */
+int engram_wkv_gate_partials(const void* x, int64_t T, int32_t K, const void* w,
+                             const uint8_t* w_scales, int32_t w_format, int32_t hc,
+                             int32_t dim, const void* hidden, const void* q_weight,
+                             const void* k_weight, void* value, float* partials,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * engram_gate -- gate and residual update.
  *   [P-rocm] _engram_gate_finish_kernel (single shard) and
  *   _engram_gate_partials_kernel; [P-common] Engram docstring and forward.
@@ -209,25 +241,27 @@ typedef struct engram_forward_args {
                                   e4m3 codes and these are its ue8m0 bytes
                                   [num_rows, head_dim / 32], as in
                                   engram_lookup_fp8 (head_dim % 32 == 0) */
-  int32_t options;         /* 0, or ENGRAM_FORWARD_GATE_EPILOGUE; other bits
+  int32_t options;         /* 0, or ENGRAM_FORWARD_STORE_KV; other bits
                               give ENGRAM_EINVAL */
 } engram_forward_args;
 
 /*
- * ENGRAM_FORWARD_GATE_EPILOGUE -- engram_forward option. Where the projection
- *   runs as a tiled GEMM (bf16 weights, or MXFP8 with T too large for the
- *   decode GEMV) and dim % 256 == 0, the GEMM's epilogue reduces each
- *   256-column key tile against hidden, q and k to the gate's per-tile sums
- *   (sum key^2, sum hidden*q*k*key over the bf16-rounded keys: the partial /
- *   finish split of [P-rocm] _engram_gate_partials_kernel /
- *   _engram_gate_finish_kernel at tile granularity) and stores only the value,
- *   so the keys never reach HBM. Elsewhere the option has no effect. Results
- *   match the default path to the rounding of the gate's sums. On MI355X at
- *   T 8192, dim 4096 both paths take the same time to within 1%: the
- *   gate's hidden reads move into the compute-bound GEMM's epilogue, where
- *   they stall it about as long as the key traffic they remove saves.
+ * Gate epilogue (the default) and ENGRAM_FORWARD_STORE_KV. Where the
+ *   projection runs as a tiled GEMM (bf16 weights, or MXFP8 with T too large
+ *   for the decode GEMV) and dim % 256 == 0, engram_forward by default has
+ *   the GEMM's epilogue reduce each 256-column key tile against hidden, q
+ *   and k to the gate's per-tile sums (sum key^2, sum hidden*q*k*key over the
+ *   bf16-rounded keys: the partial / finish split of [P-rocm]
+ *   _engram_gate_partials_kernel / _engram_gate_finish_kernel at tile
+ *   granularity, as engram_wkv_gate_partials computes) and stores only the
+ *   value, so the keys never reach HBM; a small finish kernel then forms the
+ *   gate and the update. ENGRAM_FORWARD_STORE_KV turns this off: kv is
+ *   stored whole and the plain gate kernel reads it back (the composition of
+ *   engram_wkv and engram_gate). Elsewhere the option has no effect. The two
+ *   routes agree to the rounding of the gate's sums (the same bf16 keys
+ *   summed in another order).
  */
-#define ENGRAM_FORWARD_GATE_EPILOGUE 1
+#define ENGRAM_FORWARD_STORE_KV 1
 
 size_t engram_forward_workspace_size(const engram_forward_args* a);
 int engram_forward(const engram_forward_args* a, void* workspace,

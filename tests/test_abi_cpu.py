@@ -76,7 +76,7 @@ def test_forward_args_layout_matches_c():
 
 
 def test_status_strings_and_version(lib):
-    assert lib.engram_abi_version() == 3
+    assert lib.engram_abi_version() == 4
     assert lib.engram_status_string(0) == b"ok"
     assert lib.engram_status_string(1) == b"invalid argument"
     assert lib.engram_status_string(2) == b"unsupported shape"
@@ -107,6 +107,15 @@ def test_validation_answers_before_any_launch(lib):
     assert lib.engram_lookup_fp8(0x1000, 0x2000, 10, 48, 0x3000, 16, 1, 4, 16, 0x4000, None, None) == 2
     assert lib.engram_lookup_fp8(0x1000, None, 10, 128, 0x3000, 16, 1, 4, 16, 0x4000, None, None) == 1
     assert lib.engram_lookup_fp8(0x1008, 0x2000, 10, 128, 0x3000, 16, 1, 4, 16, 0x4000, None, None) == 1
+    # fused projection + gate partials: dim % 256, hc range, then the wkv and gate checks
+    P = 0x1000
+    assert lib.engram_wkv_gate_partials(P, 4, 256, P, None, 0, 2, 200, P, P, P, P, P, None, 0, None) == 2
+    assert lib.engram_wkv_gate_partials(P, 4, 256, P, None, 0, 9, 256, P, P, P, P, P, None, 0, None) == 2
+    assert lib.engram_wkv_gate_partials(P, 4, 256, P, None, 0, 0, 256, P, P, P, P, P, None, 0, None) == 1
+    assert lib.engram_wkv_gate_partials(P, 4, 256, None, None, 0, 2, 256, P, P, P, P, P, None, 0, None) == 1
+    assert lib.engram_wkv_gate_partials(P, 4, 256, P, None, 0, 2, 256, P, P, P, P, None, None, 0, None) == 1
+    assert lib.engram_wkv_gate_partials(None, 0, 256, None, None, 0, 2, 256, None, None, None, None, None,
+                                        None, 0, None) == 0
 
 
 def test_workspace_sizes(lib):
@@ -122,7 +131,7 @@ def test_workspace_sizes(lib):
 
 
 def test_forward_rejects_unknown_options(lib):
-    """Only ENGRAM_FORWARD_GATE_EPILOGUE is a known option bit; any other is
+    """Only ENGRAM_FORWARD_STORE_KV is a known option bit; any other is
     EINVAL before any argument is looked at or anything is launched."""
     from gram_memory_layer_engram_amd import engram
 

@@ -482,20 +482,20 @@ def test_forward(name):
 
 
 @pytest.mark.parametrize("name", ["mid", "prefill", "long"])
-def test_forward_gate_epilogue_full_size(name):
-    """The gate-epilogue forward at the workloads' full sizes, in the launch
-    configuration bench.py times: sampled tokens against the oracle, masked
-    rows copied, and the same bf16 keys as the default forward (gates within
-    the reordering of their fp32 sums)."""
+def test_forward_store_kv_full_size(name):
+    """The ENGRAM_FORWARD_STORE_KV forward (kv stored whole, plain gate) at
+    the workloads' full sizes: sampled tokens against the oracle, masked rows
+    copied, and the same bf16 keys as the default gate-epilogue forward
+    (gates within the reordering of their fp32 sums)."""
     E = _E()
     inp = inputs(name)
     wl = inp["wl"]
-    _say(f"forward gate epilogue {name} T={wl.T}")
+    _say(f"forward store_kv {name} T={wl.T}")
     args = (inp["table"], inp["ids"], inp["w"], inp["w_scales"], inp["hidden"], inp["q"], inp["k"],
             inp["mask"], wl.eps, wl.clamp)
-    g_epi = torch.empty((wl.T, wl.hc), dtype=torch.float32, device=DEV)
+    g_kv = torch.empty((wl.T, wl.hc), dtype=torch.float32, device=DEV)
     g_def = torch.empty((wl.T, wl.hc), dtype=torch.float32, device=DEV)
-    out = E.forward(*args, gate_out=g_epi, gate_epilogue=True).clone()
+    out = E.forward(*args, gate_out=g_kv, store_kv=True).clone()
     E.forward(*args, gate_out=g_def)
     torch.cuda.synchronize()
     toks = sample_tokens(wl.T, SAMPLE, seed=5)
@@ -505,8 +505,8 @@ def test_forward_gate_epilogue_full_size(name):
     if inp["mask"] is not None:
         full_m = inp["mask"].cpu().numpy()
         assert np.array_equal(bits(out)[~full_m], bits(inp["hidden"])[~full_m])
-    assert np.max(np.abs(g_epi.cpu().numpy()[toks] - ref["gate"])) <= 2e-2
-    assert np.max(np.abs(g_epi.cpu().numpy() - g_def.cpu().numpy())) <= GATE_ABS
+    assert np.max(np.abs(g_kv.cpu().numpy()[toks] - ref["gate"])) <= 2e-2
+    assert np.max(np.abs(g_kv.cpu().numpy() - g_def.cpu().numpy())) <= GATE_ABS
 
 
 def test_forward_mask_none_equals_all_true_and_empty():
@@ -557,10 +557,10 @@ def test_forward_small_hidden_engram_term_dominates():
                                            ("bf16", 300, 1024, 2), ("mxfp8", 257, 1024, 3),
                                            ("mxfp8", 257, 512, 2), ("mxfp8", 200, 160, 2)])
 def test_forward_gate_epilogue_and_plain_paths(wfmt, T, dim, hc):
-    """With gate_epilogue and dim % 256 == 0 the forward runs the GEMM's gate
+    """By default, with dim % 256 == 0, the forward runs the GEMM's gate
     epilogue (key tiles reduced to per-tile partials, only the value stored);
-    without it, or at other dims, kv is stored and the plain gate runs. Both
-    against the oracle, ragged token tiles, masked tokens; each path
+    with store_kv, or at other dims, kv is stored and the plain gate runs.
+    Both against the oracle, ragged token tiles, masked tokens; each path
     bit-identical over two runs."""
     E = _E()
     g = torch.Generator(device=DEV).manual_seed(3000 + T + dim)
@@ -585,8 +585,8 @@ def test_forward_gate_epilogue_and_plain_paths(wfmt, T, dim, hc):
     gates = []
     for epi in (False, True):
         gate_out = torch.empty((T, hc), dtype=torch.float32, device=DEV)
-        out = E.forward(table, ids, w, ws, hidden, q, k, mask, gate_out=gate_out, gate_epilogue=epi).clone()
-        out2 = E.forward(table, ids, w, ws, hidden, q, k, mask, gate_epilogue=epi)
+        out = E.forward(table, ids, w, ws, hidden, q, k, mask, gate_out=gate_out, store_kv=not epi).clone()
+        out2 = E.forward(table, ids, w, ws, hidden, q, k, mask, store_kv=not epi)
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), epi
         assert_close(bf16_values(bits(out)), bf16_values(ref["out"]), *OUT_TOL, what=f"out epi={epi}")
@@ -596,6 +596,57 @@ def test_forward_gate_epilogue_and_plain_paths(wfmt, T, dim, hc):
         gates.append(gate_out.cpu().numpy())
     # both paths see the same bf16 keys; only the order of the gate's sums differs
     assert np.max(np.abs(gates[0] - gates[1])) <= 1e-3
+
+
+@pytest.mark.parametrize("wfmt,T,dim,hc", [("bf16", 300, 512, 2), ("bf16", 1, 256, 1), ("mxfp8", 257, 1024, 3),
+                                           ("mxfp8", 17, 256, 2)])
+def test_wkv_gate_partials_against_oracle_partials(wfmt, T, dim, hc):
+    """engram_wkv_gate_partials: the value block and, per 256-column key
+    tile, (sum hidden*q*k*key, sum key^2) against the oracle's partial sums
+    (the shard route of the gate) taken on the same bf16 keys, which the
+    plain projection stores; the value is bit-identical to that projection's
+    where both run the tiled GEMM."""
+    E = _E()
+    g = torch.Generator(device=DEV).manual_seed(4000 + T + dim)
+    K, N = 512, (hc + 1) * dim
+    x = (torch.randn((T, K), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    if wfmt == "bf16":
+        w = (torch.randn((N, K), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+        ws = None
+    else:
+        w = torch.randn((N, K), generator=g, device=DEV).to(torch.float8_e4m3fn).view(torch.uint8)
+        ws = (127 + torch.randint(-8, 1, (N // 32, K // 32), generator=g, device=DEV)).to(torch.uint8)
+    hidden = torch.randn((T, hc, dim), generator=g, device=DEV).to(torch.bfloat16)
+    q = (1 + 0.1 * torch.randn((hc, dim), generator=g, device=DEV)).to(torch.bfloat16)
+    k = (1 + 0.1 * torch.randn((hc, dim), generator=g, device=DEV)).to(torch.bfloat16)
+    value, part = E.wkv_gate_partials(x, w, ws, hidden, q, k)
+    kv = E.wkv(x, w, ws)
+    torch.cuda.synchronize()
+    kvb = bits(kv)
+    tiled = wfmt == "bf16" or T > 64   # engram_wkv runs the tiled GEMM too
+    if tiled:
+        assert np.array_equal(bits(value), kvb[:, hc * dim:])
+    else:
+        ref, _ = o.wkv(bits(x), u8(w), u8(ws))
+        assert_close(bf16_values(bits(value)), bf16_values(ref[:, hc * dim:]), *KV_TOL, what="value")
+    p = part.cpu().numpy()
+    hb, qb, kb = bits(hidden), bits(q), bits(k)
+    hid, qf, kf = bf16_values(hb), bf16_values(qb), bf16_values(kb)
+    key_src = kvb if tiled else bits(E.wkv(x, w, ws))  # the GEMM's keys where both are tiled
+    for i in range(dim // 256):
+        sl = slice(256 * i, 256 * i + 256)
+        cols = np.concatenate([np.arange(h * dim + 256 * i, h * dim + 256 * i + 256) for h in range(hc)]
+                              + [np.arange(hc * dim + 256 * i, hc * dim + 256 * i + 256)])
+        ks_ref, dot_ref, _ = o.gate_partials(hb, key_src[:, cols], qb, kb, 256 * i)
+        key = bf16_values(key_src[:, cols[:hc * 256]]).reshape(T, hc, 256)
+        dot_abs = np.sum(np.abs(hid[:, :, sl] * qf[None, :, sl] * kf[None, :, sl] * key), axis=2)
+        if tiled:
+            assert np.all(np.abs(p[:, :, i, 0].T - dot_ref) <= 1e-5 * dot_abs + 1e-30), i
+            assert np.all(np.abs(p[:, :, i, 1].T - ks_ref) <= 1e-5 * ks_ref + 1e-30), i
+        else:
+            # the GEMV's keys may differ from the GEMM's by bf16 rounding ties
+            assert np.all(np.abs(p[:, :, i, 0].T - dot_ref) <= 2e-2 * dot_abs + 1e-6), i
+            assert np.all(np.abs(p[:, :, i, 1].T - ks_ref) <= 2e-2 * ks_ref + 1e-6), i
 
 
 @pytest.mark.parametrize("C", [4, 3])
