@@ -14,6 +14,9 @@ the default forward launches, MFMA-bound) with its duration taken from HIP
 events on the launch stream, around calls of engram_wkv_gate_partials in the
 same launch configuration, made just before the timed steps.
 ``cpu_baseline`` is the CPU oracle on a bounded sample of the same workload.
+``measured_peaks`` are ceilings measured on the same GPU with the library's
+probes (register-only MFMA loops, a streaming read and copy of 4 GiB); each
+fraction of a datasheet peak has a ``frac_of_measured`` beside it.
 """
 
 from __future__ import annotations
@@ -195,6 +198,11 @@ def bench_decode(steps, warmup, copies=16):
     wkv_args = [(x.data_ptr(), wl.T, wl.K, st["w"].data_ptr(), st["w_scales"].data_ptr(), E.W_MXFP8, wl.N,
                  kv.data_ptr(), wws.data_ptr(), wws.numel(), sptr) for st in sets]
     t_wkv = _events_time(lambda i: L.engram_wkv(*wkv_args[i % copies]), steps, stream)
+    # the measured ceiling for that weight stream: one streaming-read launch
+    # over the same rotated copies
+    probe = E.probe_out()
+    read_args = [(st["w"].data_ptr(), st["w"].numel(), probe.data_ptr(), sptr) for st in sets]
+    t_read = _events_time(lambda i: L.engram_probe_read(*read_args[i % copies]), steps, stream)
     t_fwd = _events_time(fwd, steps, stream)
     # the single-launch variant of the same forward, same rotation
     plans_1 = [E.ForwardPlan(base["table"], s["ids"], s["w"], s["w_scales"], s["hidden"], base["q"],
@@ -202,7 +210,7 @@ def bench_decode(steps, warmup, copies=16):
     for i in range(warmup):
         plans_1[i % copies].run()
     t_one = _events_time(lambda i: plans_1[i % copies].run(), steps, stream)
-    return wl, dt, {"wkv": t_wkv, "forward": t_fwd, "single_launch": t_one}
+    return wl, dt, {"wkv": t_wkv, "forward": t_fwd, "single_launch": t_one, "read_w": t_read}
 
 
 def bench_long(steps=5, warmup=2):
@@ -230,6 +238,44 @@ def bench_long(steps=5, warmup=2):
         E.wkv(x, inp["w"], inp["w_scales"], kv=kv)
     t_wkv = _events_time(lambda i: E.wkv(x, inp["w"], inp["w_scales"], kv=kv), steps, stream)
     return wl, {"forward": t_fwd, "wkv": t_wkv}
+
+
+def measured_peaks(reps=5):
+    """Ceilings measured on this GPU with the library's probes (HIP events,
+    mean over reps launches after one warm-up): the register-only MFMA loop
+    in bf16 and MXFP8, a streaming read of 4 GiB (16 times the 256 MB
+    Infinity Cache, so HBM serves it), and 1:1 and 2:1 read/write streams
+    over the same 4 GiB."""
+    import torch
+
+    from gram_memory_layer_engram_amd import engram as E
+
+    L = E.load_library()
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    out = E.probe_out()
+    res = {}
+    for name, fmt, iters in (("mfma_bf16_TFLOPs", E.W_BF16, 20000), ("mfma_mxfp8_TFLOPs", E.W_MXFP8, 10000)):
+        flops = E.probe_mfma(fmt, iters, out)
+        t = _events_time(lambda i: E.probe_mfma(fmt, iters, out), reps, stream)
+        res[name] = round(flops / (statistics.fmean(t) * 1e-3) / 1e12, 1)
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    L.engram_probe_read(buf.data_ptr(), nbytes, out.data_ptr(), sp)
+    t = _events_time(lambda i: L.engram_probe_read(buf.data_ptr(), nbytes, out.data_ptr(), sp), reps, stream)
+    res["hbm_read_GBs"] = round(nbytes / (statistics.fmean(t) * 1e-3) / 1e9, 1)
+    # R:1 read/write streams: a copy, and 2 reads per write (the plain gate
+    # reads hidden and kv and writes out: 2.25 to 1)
+    for name, ratio in (("hbm_copy_GBs", 1), ("hbm_stream_2to1_GBs", 2)):
+        wb = nbytes // (ratio + 1) // 16 * 16
+        src, dst = buf[:ratio * wb], buf[ratio * wb:(ratio + 1) * wb]
+        args = (src.data_ptr(), dst.data_ptr(), wb, ratio, sp)
+        L.engram_probe_stream(*args)
+        t = _events_time(lambda i: L.engram_probe_stream(*args), reps, stream)
+        res[name] = round((ratio + 1) * wb / (statistics.fmean(t) * 1e-3) / 1e9, 1)
+    del buf, src, dst
+    torch.cuda.empty_cache()
+    return res
 
 
 def cpu_baseline(budget_s=12.0):
@@ -364,6 +410,16 @@ def main():
     }
 
     lwl, lkt = bench_long()
+    peaks = measured_peaks()
+    roofline["measured_peak"] = peaks["mfma_bf16_TFLOPs"]
+    roofline["frac_of_measured"] = round(achieved / peaks["mfma_bf16_TFLOPs"], 4)
+    roofline["measured_peak_source"] = "register-only bf16 MFMA loop on this GPU (engram_probe_mfma)"
+    kernels["gate_frac_of_measured_2to1"] = round(kernels["gate_GBs"] / peaks["hbm_stream_2to1_GBs"], 4)
+    d_read = statistics.fmean(dkt["read_w"]) * 1e-3
+    decode["forward_frac_of_measured_read"] = round(d_alg / d_fwd / 1e9 / peaks["hbm_read_GBs"], 4)
+    decode["read_40MiB_cold_us"] = round(d_read * 1e6, 2)
+    decode["read_40MiB_cold_GBs"] = round(dwl.N * dwl.K / d_read / 1e9, 1)
+    decode["wkv_us_vs_read_40MiB_cold"] = round(d_wkv / d_read, 3)
     l_fwd = statistics.fmean(lkt["forward"]) * 1e-3
     l_wkv = statistics.fmean(lkt["wkv"]) * 1e-3
     long = {
@@ -373,6 +429,7 @@ def main():
         "tokens_per_s": round(lwl.T / l_fwd, 1),
         "wkv_us": round(l_wkv * 1e6, 1),
         "wkv_mfma_frac": round(2.0 * lwl.T * lwl.K * lwl.N / l_wkv / 1e12 / FP8_PEAK_TFLOPS, 4),
+        "wkv_frac_of_measured_mfma": round(2.0 * lwl.T * lwl.K * lwl.N / l_wkv / 1e12 / peaks["mfma_mxfp8_TFLOPs"], 4),
     }
 
     cpu = None if a.no_cpu_baseline else cpu_baseline()
@@ -385,6 +442,7 @@ def main():
                                "bf16 tables 33556876 rows (HBM), bf16 wkv [20480, 2048], Zipf(1.1) ids, no mask",
                    "global_batch": wl.T, "parallelism": "none (1 GPU)"},
         "roofline": roofline, "kernels": kernels, "decode_t16": decode, "long_prefill": long,
+        "measured_peaks": peaks,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -345,4 +345,37 @@ int engram_forward_single_launch(const engram_forward_args* a, void* workspace,
                                           (uint32_t*)workspace, ws, (hipStream_t)stream));
 }
 
+// ---- measurement probes ----
+
+size_t engram_probe_out_bytes(void) {
+  const int blocks = probe_mfma_blocks() > probe_mem_blocks() ? probe_mfma_blocks() : probe_mem_blocks();
+  return (size_t)blocks * probe_threads() * 4;
+}
+
+int engram_probe_mfma(int32_t w_format, int32_t iters, float* out, double* flops, void* stream) {
+  if (w_format != ENGRAM_W_BF16 && w_format != ENGRAM_W_MXFP8) return ENGRAM_EINVAL;
+  if (iters <= 0 || !out || ((uintptr_t)out & 3u)) return ENGRAM_EINVAL;
+  const bool fp8 = w_format == ENGRAM_W_MXFP8;
+  if (flops)
+    *flops = (double)probe_mfma_blocks() * (probe_threads() / 64) * probe_chains() * (double)iters *
+             (fp8 ? 2.0 * 32 * 32 * 64 : 2.0 * 32 * 32 * 16);
+  return hip_status(launch_probe_mfma(fp8, iters, out, (hipStream_t)stream));
+}
+
+int engram_probe_read(const void* src, size_t bytes, uint32_t* out, void* stream) {
+  if (bytes % 16 != 0 || !out || ((uintptr_t)out & 3u)) return ENGRAM_EINVAL;
+  if (bytes == 0) return ENGRAM_OK;
+  if (!src || !aligned16(src)) return ENGRAM_EINVAL;
+  return hip_status(launch_probe_read(src, (int64_t)(bytes / 16), out, (hipStream_t)stream));
+}
+
+int engram_probe_stream(const void* src, void* dst, size_t dst_bytes, int32_t reads_per_write,
+                        void* stream) {
+  if (dst_bytes % 16 != 0 || reads_per_write < 1 || reads_per_write > 4) return ENGRAM_EINVAL;
+  if (dst_bytes == 0) return ENGRAM_OK;
+  if (!src || !dst || !aligned16(src) || !aligned16(dst)) return ENGRAM_EINVAL;
+  return hip_status(launch_probe_stream(src, dst, (int64_t)(dst_bytes / 16), reads_per_write,
+                                        (hipStream_t)stream));
+}
+
 }  // extern "C"

@@ -111,5 +111,14 @@ hipError_t launch_decode_forward(const void* table, int64_t num_rows, int head_d
                                  float clamp, void* out, float* gate_out, int32_t* err, uint32_t* sync,
                                  uint8_t* scratch, hipStream_t s);
 
+// Measurement probes (not steps of the layer): grid sizes and launchers.
+int probe_mfma_blocks();
+int probe_mem_blocks();
+int probe_threads();
+int probe_chains();
+hipError_t launch_probe_mfma(bool fp8, int iters, float* out, hipStream_t s);
+hipError_t launch_probe_read(const void* src, int64_t n16, uint32_t* out, hipStream_t s);
+hipError_t launch_probe_stream(const void* src, void* dst, int64_t n16, int ratio, hipStream_t s);
+
 
 }  // namespace engram

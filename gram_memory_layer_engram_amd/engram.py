@@ -56,6 +56,10 @@ EXPORTS = {
     "engram_forward_workspace_size": (_sz, [ctypes.POINTER(ForwardArgs)]),
     "engram_forward": (_i32, [ctypes.POINTER(ForwardArgs), _vp, _sz, _vp]),
     "engram_forward_single_launch": (_i32, [ctypes.POINTER(ForwardArgs), _vp, _sz, _vp]),
+    "engram_probe_out_bytes": (_sz, []),
+    "engram_probe_mfma": (_i32, [_i32, _i32, _vp, ctypes.POINTER(ctypes.c_double), _vp]),
+    "engram_probe_read": (_i32, [_vp, _sz, _vp, _vp]),
+    "engram_probe_stream": (_i32, [_vp, _vp, _sz, _i32, _vp]),
 }
 
 _lib = None
@@ -339,3 +343,37 @@ class ForwardPlan:
         if status:
             _check(status)
         return self.out
+
+
+# ------------------------------------------------------ measurement probes --
+
+
+def probe_out(device="cuda") -> torch.Tensor:
+    """Device words for the probes' per-thread results."""
+    n = load_library().engram_probe_out_bytes() // 4
+    return torch.empty(n, dtype=torch.int32, device=device)
+
+
+def probe_mfma(w_format: int, iters: int, out: torch.Tensor) -> float:
+    """Enqueue the register-only MFMA loop (bf16 or MXFP8); returns the flops
+    it launches. ``out`` from ``probe_out``."""
+    flops = ctypes.c_double(0.0)
+    _check(load_library().engram_probe_mfma(w_format, iters, _ptr(out), ctypes.byref(flops), _stream()))
+    return flops.value
+
+
+def probe_read(buf: torch.Tensor, out: torch.Tensor) -> None:
+    """Enqueue a streaming read of ``buf`` (dense, a multiple of 16 bytes)."""
+    _dense(buf, "buf")
+    _check(load_library().engram_probe_read(_ptr(buf), buf.numel() * buf.element_size(), _ptr(out), _stream()))
+
+
+def probe_stream(src: torch.Tensor, dst: torch.Tensor, reads_per_write: int = 1) -> None:
+    """Enqueue the R:1 streaming probe: dst (16-byte pieces) = XOR of
+    ``reads_per_write`` consecutive dst-sized blocks of src (1 = a copy)."""
+    _dense(src, "src")
+    _dense(dst, "dst")
+    nbytes = dst.numel() * dst.element_size()
+    if src.numel() * src.element_size() != reads_per_write * nbytes:
+        raise ValueError("probe_stream: src must hold reads_per_write times dst's bytes")
+    _check(load_library().engram_probe_stream(_ptr(src), _ptr(dst), nbytes, reads_per_write, _stream()))

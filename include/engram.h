@@ -293,6 +293,47 @@ int engram_forward(const engram_forward_args* a, void* workspace,
 int engram_forward_single_launch(const engram_forward_args* a, void* workspace,
                                  size_t workspace_bytes, void* stream);
 
+/*
+ * Measurement probes. Not steps of the layer: they measure the rates this
+ * chip sustains, so that each kernel's achieved rate can be quoted against a
+ * measured ceiling as well as against the datasheet peak. Asynchronous on
+ * `stream` like the rest; time them with events.
+ *
+ * engram_probe_out_bytes -- bytes of device memory `out` must hold for
+ *   engram_probe_mfma and engram_probe_read (4-byte words: one per thread
+ *   of the MFMA probe, 1024 per compute unit; depends on the device's
+ *   compute-unit count).
+ *
+ * engram_probe_mfma -- a register-only loop of independent MFMA chains on
+ *   every compute unit: v_mfma_f32_32x32x16_bf16 (ENGRAM_W_BF16, operands
+ *   bf16 2^-8) or the scaled v_mfma_scale_f32_32x32x64_f8f6f4 (ENGRAM_W_MXFP8,
+ *   e4m3 1.0 with E8M0 scale 2^0), `iters` steps of 8 MFMAs per wave. Each
+ *   thread stores the sum of its 128 accumulators to out[thread]: exactly
+ *   128 * iters * 2^-12 (bf16) or 128 * 64 * iters (MXFP8) while that is
+ *   below 2^24. *flops (host, nullable) receives the flop count launched.
+ *   ENGRAM_EINVAL for another format, iters <= 0, or a NULL / misaligned out.
+ *
+ * engram_probe_read -- streams `bytes` (a multiple of 16) from device memory
+ *   `src` (16-byte aligned) in 16-byte pieces: one pass of workgroups that
+ *   covers the buffer, each thread issuing its 4 loads before it uses any.
+ *   Each wave XORs the words it read into one word of out (wave index
+ *   modulo out's words) with an atomic XOR, so, with out zeroed first, the
+ *   XOR of all of out's words is the XOR of the buffer.
+ *
+ * engram_probe_stream -- a streaming read/write at a fixed ratio: dst
+ *   (dst_bytes, a multiple of 16) receives, per 16-byte piece d, the XOR of
+ *   src pieces j*(dst_bytes/16) + d for j < reads_per_write (1..4; 1 is a
+ *   copy), so src holds reads_per_write * dst_bytes; one pass of workgroups,
+ *   each thread loading 2 pieces of every read stream before its stores.
+ *   Both 16-byte aligned, not overlapping. ENGRAM_EINVAL otherwise;
+ *   dst_bytes = 0 is a no-op.
+ */
+size_t engram_probe_out_bytes(void);
+int engram_probe_mfma(int32_t w_format, int32_t iters, float* out, double* flops, void* stream);
+int engram_probe_read(const void* src, size_t bytes, uint32_t* out, void* stream);
+int engram_probe_stream(const void* src, void* dst, size_t dst_bytes, int32_t reads_per_write,
+                        void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -116,6 +116,17 @@ def test_validation_answers_before_any_launch(lib):
     assert lib.engram_wkv_gate_partials(P, 4, 256, P, None, 0, 2, 256, P, P, P, P, None, None, 0, None) == 1
     assert lib.engram_wkv_gate_partials(None, 0, 256, None, None, 0, 2, 256, None, None, None, None, None,
                                         None, 0, None) == 0
+    # measurement probes: argument checks only (a valid call would launch)
+    assert lib.engram_probe_mfma(7, 10, P, None, None) == 1        # unknown format
+    assert lib.engram_probe_mfma(0, 0, P, None, None) == 1         # iters <= 0
+    assert lib.engram_probe_mfma(0, 10, None, None, None) == 1     # no out
+    assert lib.engram_probe_read(P, 17, P, None) == 1              # not a multiple of 16
+    assert lib.engram_probe_read(None, 0, P, None) == 0            # empty: no launch
+    assert lib.engram_probe_read(0x1008, 32, P, None) == 1         # misaligned source
+    assert lib.engram_probe_stream(None, None, 0, 1, None) == 0
+    assert lib.engram_probe_stream(P, 0x2008, 32, 1, None) == 1    # misaligned destination
+    assert lib.engram_probe_stream(P, 0x2000, 32, 5, None) == 1    # ratio outside 1..4
+    assert lib.engram_probe_stream(P, 0x2000, 24, 1, None) == 1    # not a multiple of 16
 
 
 def test_workspace_sizes(lib):
