@@ -237,7 +237,15 @@ def bench_long(steps=5, warmup=2):
     for _ in range(warmup):
         E.wkv(x, inp["w"], inp["w_scales"], kv=kv)
     t_wkv = _events_time(lambda i: E.wkv(x, inp["w"], inp["w_scales"], kv=kv), steps, stream)
-    return wl, {"forward": t_fwd, "wkv": t_wkv}
+    # the MXFP8 activation quantize alone (engram_mx_quantize) on the same rows
+    xq = torch.empty((wl.T, wl.K), dtype=torch.uint8, device="cuda")
+    xs = torch.empty((wl.T, wl.K // 32), dtype=torch.uint8, device="cuda")
+    L = E.load_library()
+    qargs = (x.data_ptr(), wl.T, wl.K, xq.data_ptr(), xs.data_ptr(), stream.cuda_stream)
+    if L.engram_mx_quantize(*qargs) != 0:
+        raise RuntimeError("engram_mx_quantize refused the long-prefill rows")
+    t_q = _events_time(lambda i: L.engram_mx_quantize(*qargs), max(steps, 20), stream)
+    return wl, {"forward": t_fwd, "wkv": t_wkv, "mx_quantize": t_q}
 
 
 def measured_peaks(reps=5):
@@ -422,6 +430,7 @@ def main():
     decode["wkv_us_vs_read_40MiB_cold"] = round(d_wkv / d_read, 3)
     l_fwd = statistics.fmean(lkt["forward"]) * 1e-3
     l_wkv = statistics.fmean(lkt["wkv"]) * 1e-3
+    l_q = statistics.fmean(lkt["mx_quantize"]) * 1e-3
     long = {
         "workload": "long prefill T=32768, dim 7168, hc 4, K 3072, MXFP8 wkv [35840, 3072], Zipf ids, "
                     "10% masked",
@@ -430,6 +439,11 @@ def main():
         "wkv_us": round(l_wkv * 1e6, 1),
         "wkv_mfma_frac": round(2.0 * lwl.T * lwl.K * lwl.N / l_wkv / 1e12 / FP8_PEAK_TFLOPS, 4),
         "wkv_frac_of_measured_mfma": round(2.0 * lwl.T * lwl.K * lwl.N / l_wkv / 1e12 / peaks["mfma_mxfp8_TFLOPs"], 4),
+        # activation quantize: per token 2K bytes read, K + K/32 written
+        "mx_quantize_us": round(l_q * 1e6, 2),
+        "mx_quantize_GBs": round(lwl.T * (3 * lwl.K + lwl.K // 32) / l_q / 1e9, 1),
+        "mx_quantize_frac_of_measured_2to1": round(lwl.T * (3 * lwl.K + lwl.K // 32) / l_q / 1e9
+                                                   / peaks["hbm_stream_2to1_GBs"], 4),
     }
 
     cpu = None if a.no_cpu_baseline else cpu_baseline()
