@@ -116,6 +116,8 @@ def test_validation_answers_before_any_launch(lib):
     assert lib.engram_wkv_gate_partials(P, 4, 256, P, None, 0, 2, 256, P, P, P, P, None, None, 0, None) == 1
     assert lib.engram_wkv_gate_partials(None, 0, 256, None, None, 0, 2, 256, None, None, None, None, None,
                                         None, 0, None) == 0
+    # MXFP8 needs its workspace (x's codes and scales): none given -> EINVAL
+    assert lib.engram_wkv_gate_partials(P, 4, 256, P, P, 1, 2, 256, P, P, P, P, P, None, 0, None) == 1
     # measurement probes: argument checks only (a valid call would launch)
     assert lib.engram_probe_mfma(7, 10, P, None, None) == 1        # unknown format
     assert lib.engram_probe_mfma(0, 0, P, None, None) == 1         # iters <= 0

@@ -598,17 +598,19 @@ def test_forward_gate_epilogue_and_plain_paths(wfmt, T, dim, hc):
     assert np.max(np.abs(gates[0] - gates[1])) <= 1e-3
 
 
-@pytest.mark.parametrize("wfmt,T,dim,hc", [("bf16", 300, 512, 2), ("bf16", 1, 256, 1), ("mxfp8", 257, 1024, 3),
-                                           ("mxfp8", 17, 256, 2)])
-def test_wkv_gate_partials_against_oracle_partials(wfmt, T, dim, hc):
+@pytest.mark.parametrize("wfmt,T,dim,hc,K", [("bf16", 300, 512, 2, 512), ("bf16", 1, 256, 1, 512),
+                                             ("mxfp8", 257, 1024, 3, 512), ("mxfp8", 17, 256, 2, 512),
+                                             ("bf16", 130, 256, 2, 520), ("mxfp8", 100, 512, 2, 384)])
+def test_wkv_gate_partials_against_oracle_partials(wfmt, T, dim, hc, K):
     """engram_wkv_gate_partials: the value block and, per 256-column key
     tile, (sum hidden*q*k*key, sum key^2) against the oracle's partial sums
     (the shard route of the gate) taken on the same bf16 keys, which the
     plain projection stores; the value is bit-identical to that projection's
-    where both run the tiled GEMM."""
+    where both run the tiled GEMM. K = 520 takes the bf16 kernel's ragged
+    last k-stage, K = 384 the MXFP8 kernel for K % 512 != 0."""
     E = _E()
-    g = torch.Generator(device=DEV).manual_seed(4000 + T + dim)
-    K, N = 512, (hc + 1) * dim
+    g = torch.Generator(device=DEV).manual_seed(4000 + T + dim + K)
+    N = (hc + 1) * dim
     x = (torch.randn((T, K), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
     if wfmt == "bf16":
         w = (torch.randn((N, K), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
