@@ -27,47 +27,10 @@ namespace engram {
 
 namespace {
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x3 __attribute__((ext_vector_type(3)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
 __device__ __forceinline__ i32x8 cat(const uint4& lo, const uint4& hi) {
   const i32x4 a = __builtin_bit_cast(i32x4, lo);
   const i32x4 b = __builtin_bit_cast(i32x4, hi);
   return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
-}
-
-// The E8M0 bytes of one wave's k-steps in one scale row: word s holds the
-// bytes of k blocks (step0+s)*4 .. +3, lane group g uses byte g. When all SPW
-// steps exist the SPW words come in one multi-dword load (4-byte aligned:
-// K % 128 == 0); otherwise one word per existing step, so nothing is read
-// past the row's last k block.
-template <int SPW>
-__device__ __forceinline__ void scale_words(const uint8_t* row, int step0, int nsteps, uint32_t (&wd)[SPW]) {
-  const uint32_t* p = reinterpret_cast<const uint32_t*>(row + step0 * 4);
-  if (step0 + SPW <= nsteps) {
-    if constexpr (SPW == 1) {
-      wd[0] = p[0];
-    } else if constexpr (SPW == 2) {
-      u32x2 v;
-      __builtin_memcpy(&v, p, 8);
-      wd[0] = v.x; wd[1] = v.y;
-    } else if constexpr (SPW == 3) {
-      u32x3 v;
-      __builtin_memcpy(&v, p, 12);
-      wd[0] = v.x; wd[1] = v.y; wd[2] = v.z;
-    } else {
-      u32x4 v;
-      __builtin_memcpy(&v, p, 16);
-      wd[0] = v.x; wd[1] = v.y; wd[2] = v.z; wd[3] = v.w;
-    }
-  } else {
-#pragma unroll
-    for (int s = 0; s < SPW; ++s) {
-      wd[s] = 0;
-      if (step0 + s < nsteps) wd[s] = p[s];
-    }
-  }
 }
 
 // ------------------------------------------------------------------ GEMV --
@@ -101,7 +64,7 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_mxfp8_kernel(
   // compiler from moving it next to its use; a padding token reloads token
   // 0 (its MFMA column only feeds outputs that are not stored).
   uint4 wlo[RT][SPW], whi[RT][SPW];
-  uint32_t wsw[RT][SPW];
+  int wsc[RT][SPW];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt) {
     const int nrow = n0 + rt * 16;
@@ -109,16 +72,17 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_mxfp8_kernel(
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
       wlo[rt][s] = whi[rt][s] = make_uint4(0, 0, 0, 0);
+      wsc[rt][s] = 0;
       if (step0 + s < nsteps) {
         const int kbyte = (step0 + s) * 128 + 16 * g;
         wlo[rt][s] = *reinterpret_cast<const uint4*>(wrow + kbyte);
         whi[rt][s] = *reinterpret_cast<const uint4*>(wrow + kbyte + 64);
+        wsc[rt][s] = ws[(nrow / 32) * kb + (step0 + s) * 4 + g];
       }
     }
-    scale_words<SPW>(ws + (nrow / 32) * kb, step0, nsteps, wsw[rt]);
   }
   uint4 xlo[NT][SPW], xhi[NT][SPW];
-  uint32_t xsw[NT][SPW];
+  int xsc[NT][SPW];
 #pragma unroll
   for (int j = 0; j < NT; ++j) {
     const int t = j * 16 + r < T ? j * 16 + r : 0;
@@ -126,13 +90,14 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_mxfp8_kernel(
 #pragma unroll
     for (int s = 0; s < SPW; ++s) {
       xlo[j][s] = xhi[j][s] = make_uint4(0, 0, 0, 0);
+      xsc[j][s] = 0;
       if (step0 + s < nsteps) {
         const int kbyte = (step0 + s) * 128 + 16 * g;
         xlo[j][s] = *reinterpret_cast<const uint4*>(xrow + kbyte);
         xhi[j][s] = *reinterpret_cast<const uint4*>(xrow + kbyte + 64);
+        xsc[j][s] = xs[(int64_t)t * kb + (step0 + s) * 4 + g];
       }
     }
-    scale_words<SPW>(xs + (int64_t)t * kb, step0, nsteps, xsw[j]);
   }
 
   f32x4 acc[RT][NT];
@@ -150,8 +115,7 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_mxfp8_kernel(
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
         acc[rt][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
-            cat(wlo[rt][s], whi[rt][s]), xb, acc[rt][j], 0, 0, 0, (int)((wsw[rt][s] >> (8 * g)) & 0xffu), 0,
-            (int)((xsw[j][s] >> (8 * g)) & 0xffu));
+            cat(wlo[rt][s], whi[rt][s]), xb, acc[rt][j], 0, 0, 0, wsc[rt][s], 0, xsc[j][s]);
     }
   }
 
