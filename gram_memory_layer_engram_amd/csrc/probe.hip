@@ -137,11 +137,6 @@ __global__ __launch_bounds__(PROBE_THREADS) void stream_probe_kernel(const uint4
   }
 }
 
-}  // namespace
-
-int probe_mfma_blocks() { return dev_info().num_cus * PROBE_MFMA_WG_PER_CU; }
-int probe_mem_blocks() { return dev_info().num_cus * PROBE_OUT_WG_PER_CU; }
-
 // Workgroups for one pass over n16 pieces at `unroll` pieces per thread
 // (capped at 2^30; past that the threads loop).
 int64_t mem_grid(int64_t n16, int unroll) {
@@ -149,6 +144,12 @@ int64_t mem_grid(int64_t n16, int unroll) {
   const int64_t b = (n16 + per_block - 1) / per_block;
   return b < 1 ? 1 : (b > (1 << 30) ? (1 << 30) : b);
 }
+
+}  // namespace
+
+int probe_mfma_blocks() { return dev_info().num_cus * PROBE_MFMA_WG_PER_CU; }
+int probe_mem_blocks() { return dev_info().num_cus * PROBE_OUT_WG_PER_CU; }
+
 int probe_threads() { return PROBE_THREADS; }
 int probe_chains() { return PROBE_CHAINS; }
 
