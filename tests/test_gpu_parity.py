@@ -146,9 +146,10 @@ def test_lookup_strided_ids_and_bad_ids():
     assert np.array_equal(bits(rows), want)
 
 
-@pytest.mark.parametrize("hd", [8, 32, 64, 128, 96])
+@pytest.mark.parametrize("hd", [8, 32, 64, 128, 96, 1024])
 @pytest.mark.parametrize("T", [1, 17, 65, 1000])
 def test_lookup_shapes(hd, T):
+    """Row widths from the smallest (8) to the largest the gather takes (1024)."""
     E = _E()
     g = torch.Generator(device=DEV).manual_seed(hd * 1000 + T)
     R, C = 5003, 7
