@@ -524,6 +524,39 @@ def test_forward_mask_none_equals_all_true_and_empty():
     assert out.shape == (0, wl.hc, wl.dim)
 
 
+@pytest.mark.parametrize("wfmt,T,dim,hc,route", [("bf16", 300, 512, 2, "default"), ("bf16", 300, 512, 2, "store_kv"),
+                                                 ("mxfp8", 16, 1024, 2, "default"), ("mxfp8", 16, 1024, 2, "single")])
+def test_forward_all_tokens_masked_pass_through(wfmt, T, dim, hc, route):
+    """Every token masked: the output is hidden bit for bit (NaN, infinities
+    and -0.0 included: masked positions pass through untouched) and every
+    gate is 0, on the gate-epilogue, store-kv, decode GEMV and single-launch
+    routes."""
+    E = _E()
+    g = torch.Generator(device=DEV).manual_seed(5000 + T + dim)
+    R, C, hd = 2503, 8, 128
+    K, N = C * hd, (hc + 1) * dim
+    table = (torch.randn((R, hd), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    ids = torch.randint(0, R, (T, C), generator=g, device=DEV, dtype=torch.int32)
+    if wfmt == "bf16":
+        w = (torch.randn((N, K), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+        ws = None
+    else:
+        w = torch.randn((N, K), generator=g, device=DEV).to(torch.float8_e4m3fn).view(torch.uint8)
+        ws = (127 + torch.randint(-8, 1, (N // 32, K // 32), generator=g, device=DEV)).to(torch.uint8)
+    hidden = torch.randn((T, hc, dim), generator=g, device=DEV).to(torch.bfloat16)
+    hv = hidden.view(torch.int16).view(-1)
+    hv[0:4] = torch.tensor([0x7FC0, 0x7F80, 0xFF80 - 0x10000, 0x8000 - 0x10000], dtype=torch.int16, device=DEV)
+    q = (1 + 0.1 * torch.randn((hc, dim), generator=g, device=DEV)).to(torch.bfloat16)
+    k = (1 + 0.1 * torch.randn((hc, dim), generator=g, device=DEV)).to(torch.bfloat16)
+    mask = torch.zeros((T,), dtype=torch.bool, device=DEV)
+    gate_out = torch.full((T, hc), 7.0, dtype=torch.float32, device=DEV)
+    out = E.forward(table, ids, w, ws, hidden, q, k, mask, gate_out=gate_out, store_kv=route == "store_kv",
+                    single_launch=route == "single")
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), hidden.view(torch.int16))
+    assert torch.all(gate_out == 0)
+
+
 def test_forward_zero_value_returns_hidden():
     E = _E()
     inp = inputs("tiny")
