@@ -33,8 +33,9 @@ typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // The same rounding in one instruction (v_cvt_pk_bf16_f32: round to nearest,
 // ties to even; identical to pack_bf16x2 for every non-NaN input, a NaN
-// becomes the hardware's quiet NaN). For the GEMM epilogue, where the
-// conversion of a whole tile sits between the last MFMA and the stores.
+// becomes the hardware's quiet NaN). Used where the conversion is on the
+// critical path: the GEMM epilogue (a whole tile between the last MFMA and
+// the stores) and the gate's output rows.
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   const f32x2_t v = {lo, hi};
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));

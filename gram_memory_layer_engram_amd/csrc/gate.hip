@@ -184,10 +184,10 @@ __global__ __launch_bounds__(BS) void gate_kernel(
         unpack8(hv, a);
         unpack8(vreg[c], v);
         uint4 o;
-        o.x = pack_bf16x2(fmaf(g, v[0], a[0]), fmaf(g, v[1], a[1]));
-        o.y = pack_bf16x2(fmaf(g, v[2], a[2]), fmaf(g, v[3], a[3]));
-        o.z = pack_bf16x2(fmaf(g, v[4], a[4]), fmaf(g, v[5], a[5]));
-        o.w = pack_bf16x2(fmaf(g, v[6], a[6]), fmaf(g, v[7], a[7]));
+        o.x = cvt_pk_bf16(fmaf(g, v[0], a[0]), fmaf(g, v[1], a[1]));
+        o.y = cvt_pk_bf16(fmaf(g, v[2], a[2]), fmaf(g, v[3], a[3]));
+        o.z = cvt_pk_bf16(fmaf(g, v[4], a[4]), fmaf(g, v[5], a[5]));
+        o.w = cvt_pk_bf16(fmaf(g, v[6], a[6]), fmaf(g, v[7], a[7]));
         orow[h * dim8 + j] = o;
       }
     }
@@ -308,10 +308,10 @@ __global__ __launch_bounds__(BS) void gate_exact_kernel(
     float a[8];
     unpack8(hv[h], a);
     uint4 o;
-    o.x = pack_bf16x2(fmaf(g, v[0], a[0]), fmaf(g, v[1], a[1]));
-    o.y = pack_bf16x2(fmaf(g, v[2], a[2]), fmaf(g, v[3], a[3]));
-    o.z = pack_bf16x2(fmaf(g, v[4], a[4]), fmaf(g, v[5], a[5]));
-    o.w = pack_bf16x2(fmaf(g, v[6], a[6]), fmaf(g, v[7], a[7]));
+    o.x = cvt_pk_bf16(fmaf(g, v[0], a[0]), fmaf(g, v[1], a[1]));
+    o.y = cvt_pk_bf16(fmaf(g, v[2], a[2]), fmaf(g, v[3], a[3]));
+    o.z = cvt_pk_bf16(fmaf(g, v[4], a[4]), fmaf(g, v[5], a[5]));
+    o.w = cvt_pk_bf16(fmaf(g, v[6], a[6]), fmaf(g, v[7], a[7]));
     if (!active) o = hv[h];   // masked: hidden, bit for bit
     orow[h * dim8 + tid] = o;
   }
