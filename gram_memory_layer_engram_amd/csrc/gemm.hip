@@ -202,57 +202,78 @@ __device__ __forceinline__ void store_tile(f32x16 (&acc)[4][4], char* smem, uint
     }
     return;
   }
-  // key tile of copy h, columns d0 .. d0+255 of that copy
+  // key tile of copy h, columns d0 .. d0+255 of that copy. Lane group g =
+  // lane/16 of wave w takes rows t = 64w + 4r + g (r = 0..15: the four
+  // groups read consecutive rows, which the LDS swizzle keeps on distinct
+  // banks); lane c16 = lane%16 takes the 16-byte pieces c16 and 16 + c16 of
+  // each row (columns 8*c16.. and 128 + 8*c16..), so a load instruction
+  // covers 256 contiguous bytes of four rows.
   const int h = n0 / ep.dim, d0 = n0 - h * ep.dim;
-  const int d = d0 + c * 8;
-  float qk[8];
+  const int g = lane >> 4, c16 = lane & 15;
+  float qk[16];
   {
-    const uint4 q8 = *reinterpret_cast<const uint4*>(ep.q + h * ep.dim + d);
-    const uint4 k8 = *reinterpret_cast<const uint4*>(ep.k + h * ep.dim + d);
-    const uint32_t qw[4] = {q8.x, q8.y, q8.z, q8.w}, kw[4] = {k8.x, k8.y, k8.z, k8.w};
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      qk[2 * e] = bf16lo(qw[e]) * bf16lo(kw[e]);
-      qk[2 * e + 1] = bf16hi(qw[e]) * bf16hi(kw[e]);
+    for (int half = 0; half < 2; ++half) {
+      const int d = d0 + half * 128 + c16 * 8;
+      const uint4 q8 = *reinterpret_cast<const uint4*>(ep.q + h * ep.dim + d);
+      const uint4 k8 = *reinterpret_cast<const uint4*>(ep.k + h * ep.dim + d);
+      const uint32_t qw[4] = {q8.x, q8.y, q8.z, q8.w}, kw[4] = {k8.x, k8.y, k8.z, k8.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        qk[half * 8 + 2 * e] = bf16lo(qw[e]) * bf16lo(kw[e]);
+        qk[half * 8 + 2 * e + 1] = bf16hi(qw[e]) * bf16hi(kw[e]);
+      }
     }
   }
   const int tiles = ep.dim / 256, tile = d0 / 256;
   // all 32 hidden pieces of this thread in flight at once (the accumulators
   // are dead, their registers free), then the reductions
-  uint4 hid[32];
+  uint4 hid[16][2];
 #pragma unroll
-  for (int it = 0; it < 32; ++it) {
-    const int t = wave * 64 + it * 2 + (lane >> 5);
-    hid[it] = make_uint4(0, 0, 0, 0);
-    if (t0 + t < T) hid[it] = *reinterpret_cast<const uint4*>(ep.hidden + ((int64_t)(t0 + t) * ep.hc + h) * ep.dim + d);
+  for (int r = 0; r < 16; ++r) {
+    const int t = wave * 64 + 4 * r + g;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      hid[r][half] = make_uint4(0, 0, 0, 0);
+      if (t0 + t < T)
+        hid[r][half] = *reinterpret_cast<const uint4*>(ep.hidden + ((int64_t)(t0 + t) * ep.hc + h) * ep.dim + d0 +
+                                                       half * 128 + c16 * 8);
+    }
   }
-  // per-lane sums of this lane's 8 columns, one pair per row (iteration it)
-  float dts[32], kss[32];
+  // per-lane sums of this lane's 16 columns, one pair per row r
+  float dts[16], kss[16];
 #pragma unroll
-  for (int it = 0; it < 32; ++it) {
-    const int t = wave * 64 + it * 2 + (lane >> 5);
-    const uint4 kv8 = lds_row(t);
-    const uint4 h8 = hid[it];
-    const uint32_t kw[4] = {kv8.x, kv8.y, kv8.z, kv8.w}, hw[4] = {h8.x, h8.y, h8.z, h8.w};
+  for (int r = 0; r < 16; ++r) {
+    const int t = wave * 64 + 4 * r + g;
     float dt = 0.f, ks = 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float k0 = bf16lo(kw[e]), k1 = bf16hi(kw[e]);
-      ks = fmaf(k0, k0, ks);
-      ks = fmaf(k1, k1, ks);
-      dt = fmaf(bf16lo(hw[e]) * qk[2 * e], k0, dt);
-      dt = fmaf(bf16hi(hw[e]) * qk[2 * e + 1], k1, dt);
-    }
-    dts[it] = dt;
-    kss[it] = ks;
-  }
-  // Sum over the 32 lanes of each half-wave for all 32 rows at once: at
-  // each step lane c keeps the half of its rows selected by bit w of c and
-  // adds the partner's (lane c^w) copy of them, so 31 exchanges per sum
-  // instead of 5 per row; lane c ends with row it = c, in a fixed order.
+    for (int half = 0; half < 2; ++half) {
+      const int ch = half * 16 + c16;
+      const uint4 kv8 = *reinterpret_cast<const uint4*>(smem + t * 512 + ((ch ^ (t & 31)) << 4));
+      const uint4 h8 = hid[r][half];
+      const uint32_t kw[4] = {kv8.x, kv8.y, kv8.z, kv8.w}, hw[4] = {h8.x, h8.y, h8.z, h8.w};
 #pragma unroll
-  for (int w = 16; w >= 1; w >>= 1) {
-    const bool upper = (c & w) != 0;
+      for (int e = 0; e < 4; ++e) {
+        const float k0 = bf16lo(kw[e]), k1 = bf16hi(kw[e]);
+        ks = fmaf(k0, k0, ks);
+        ks = fmaf(k1, k1, ks);
+        dt = fmaf(bf16lo(hw[e]) * qk[half * 8 + 2 * e], k0, dt);
+        dt = fmaf(bf16hi(hw[e]) * qk[half * 8 + 2 * e + 1], k1, dt);
+      }
+    }
+    dts[r] = dt;
+    kss[r] = ks;
+  }
+  // Sum over the 16 lanes of each group for all 16 rows at once: at each
+  // step lane c16 keeps the half of its rows selected by bit w of c16 and
+  // adds the partner's (lane c16^w) copy of them, so 15 exchanges per sum;
+  // lane c16 ends with row r = c16, in a fixed order. (With 32 lanes per row
+  // the exchanges double, 62 shuffles against 30: 633 -> 625 us at the
+  // prefill shape; 8 lanes per row, 14 shuffles but 128-byte row pieces per
+  // load, measured 642 us.)
+#pragma unroll
+  for (int w = 8; w >= 1; w >>= 1) {
+    const bool upper = (c16 & w) != 0;
 #pragma unroll
     for (int i = 0; i < w; ++i) {
       const float rd = __shfl_xor(upper ? dts[i] : dts[i + w], w, 64);
@@ -261,7 +282,7 @@ __device__ __forceinline__ void store_tile(f32x16 (&acc)[4][4], char* smem, uint
       kss[i] = (upper ? kss[i + w] : kss[i]) + rk;
     }
   }
-  const int t = wave * 64 + c * 2 + (lane >> 5);
+  const int t = wave * 64 + 4 * c16 + g;
   if (t0 + t < T) ep.part[((int64_t)h * T + t0 + t) * tiles + tile] = make_float2(dts[0], kss[0]);
 }
 
