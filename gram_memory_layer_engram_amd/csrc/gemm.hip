@@ -24,16 +24,21 @@
 //    ragged tiles need no branches; a stage that does not exist is loaded
 //    from an offset past the range (zeros into a buffer nobody reads), which
 //    keeps the loop free of branches.
-//  * bf16: a k stage is 32 elements (64-byte LDS rows of 4 pieces, piece p of
-//    row r at p ^ ((r >> 2) & 3), conflict-free for the 32-row fragment
-//    reads). Four stages (128 KiB); the loads of stage k+3 are spread over
-//    stage k, one DMA per 4 MFMAs, so the address unit sees a steady stream
-//    instead of bursts that stall the issuing wave. The barrier that
-//    publishes stage k+1 sits after the first 4 of the last 16 MFMAs of
-//    stage k, and the next stage's first fragments are read under the other
+//  * bf16: a k slice is 64 elements, so one DMA instruction fetches 8 rows x
+//    128 bytes, 8 whole cache lines (with 32-element stages it touched half
+//    of 16 lines: 627 -> 564 us for the prefill GEMM, same instructions,
+//    same bytes). LDS rows are 128 bytes of 8 pieces, piece p of row r at
+//    p ^ ((r >> 1) & 7), conflict-free for the 32-row fragment reads. Each
+//    operand's slice is a 32 KiB chunk in a ring of five (160 KiB, all of
+//    LDS): during slice d, B of slice d+1 is fetched first (one DMA per 2
+//    MFMAs), then A of slice d+2 (one per 4), so every DMA has at least ~38
+//    MFMAs before the barrier that needs it (32 already suffice: a
+//    three-stage ring times like a four-stage one). The barrier that
+//    publishes slice d+1 sits after the first 4 of the last 16 MFMAs of
+//    slice d, and the next slice's first fragments are read under the other
 //    12.
-//  * MXFP8 (K % 512 == 0, K <= 3584): the bf16 pipeline with 64-e4m3 stages
-//    (gemm_mx_paced_kernel, described above it). Other K: a plain two-stage
+//  * MXFP8 (K % 512 == 0, K <= 3584): a four-stage pipeline of 64-e4m3
+//    stages (gemm_mx_paced_kernel, described above it). Other K: a plain two-stage
 //    kernel with 128-byte k stages (piece p of row r at p ^ ((r >> 1) & 7)).
 //  * Epilogue: the bf16 tile is staged in LDS as [token][n] (512-byte rows,
 //    16-byte chunks XOR-swizzled by token) and written back as whole rows,
@@ -67,7 +72,7 @@ constexpr int ROW_BYTES = 128;
 constexpr int PIECES = ROW_BYTES / 16;
 constexpr int TILE_BYTES = BM * ROW_BYTES;       // 32 KiB
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;      // A + B
-// bf16: 64-byte k stages (32 elements), four of them
+// paced MXFP8: 64-byte k stages, four of them
 constexpr int H_ROW = 64;
 constexpr int H_TILE = BM * H_ROW;               // 16 KiB
 constexpr int H_STAGE = 2 * H_TILE;
@@ -75,6 +80,15 @@ constexpr int H_STAGES = 4;
 constexpr int H_DMA = 8;                         // DMA instructions per wave per stage
 static_assert(H_STAGES * H_STAGE == LDS_BYTES && 2 * STAGE_BYTES == LDS_BYTES, "LDS budget");
 static_assert(BN * 512 == LDS_BYTES, "epilogue staging tile");
+// bf16: 64-element k slices (128-byte LDS rows of 8 pieces, piece p of row
+// r at p ^ ((r >> 1) & 7)); each operand's slice is a 32 KiB chunk in a ring
+// of five
+constexpr int Q_ROW = 128;
+constexpr int Q_CHUNK = BM * Q_ROW;
+constexpr int Q_SLOTS = 5;
+constexpr int Q_LDS = Q_SLOTS * Q_CHUNK;         // 160 KiB
+constexpr int Q_DMA = Q_CHUNK / (THREADS * 16);  // DMA instructions per wave per chunk
+static_assert(Q_DMA == 8 && Q_LDS >= LDS_BYTES, "bf16 ring");
 constexpr int GROUP_T = 4;
 constexpr uint32_t RSRC_FLAGS = 0x00020000u;
 
@@ -286,7 +300,7 @@ __device__ __forceinline__ void store_tile(f32x16 (&acc)[4][4], char* smem, uint
   if (t0 + t < T) ep.part[((int64_t)h * T + t0 + t) * tiles + tile] = make_float2(dts[0], kss[0]);
 }
 
-// bf16 wkv GEMM (see the file comment). KTAIL: K % 32 != 0, the last stage's
+// bf16 wkv GEMM (see the file comment). KTAIL: K % 64 != 0, the last slice's
 // pieces past the row end are loaded from past the range (zeros).
 template <bool KTAIL>
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -303,26 +317,18 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ x, int T, int K, const uint16
   const rsrc_t ra = make_rsrc(w + (int64_t)n0 * K, (uint32_t)min(BM, N - n0) * row_bytes);
   const rsrc_t rb = make_rsrc(x + (int64_t)t0 * K, (uint32_t)min(BN, T - t0) * row_bytes);
   const uint32_t oob = (uint32_t)BM * row_bytes;   // at or past both ranges
-  const int nk = (K + 31) / 32;
+  const int nk = (K + 63) / 64;
 
-  // DMA i of an operand (i = 0..3): LDS rows 16*(wave + 4i) .. +16, lane l
-  // fetching row 16*(wave+4i) + l/4, piece (l%4) ^ ((row >> 2) & 3).
-  uint32_t doff[4], pofs[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (wave + 4 * i) * 16 + (lane >> 2);
-    pofs[i] = (uint32_t)(((lane & 3) ^ ((r >> 2) & 3)) * 16);
-    doff[i] = (uint32_t)r * row_bytes + pofs[i];
-  }
-  // DMA j (0..7) of a stage: operand j & 1, block j >> 1; stage byte offset kofs
-  auto dma = [&](int buf, uint32_t kofs, int j) {
-    const int i = j >> 1, op = j & 1;
-    uint32_t off = doff[i] + kofs;
-    if (KTAIL && kofs + pofs[i] >= row_bytes) off = oob;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? rb : ra,
-                                             (lds_ptr_t)(smem + buf * H_STAGE + op * H_TILE +
-                                                         (wave + 4 * i) * 1024),
-                                             16, off, 0, 0, 0);
+  // DMA i (0..7) of a chunk: LDS rows 8*(wave + 4i) .. +8, lane l fetching
+  // row 8*(wave + 4i) + l/8, piece (l%8) ^ ((row >> 1) & 7); that swizzle
+  // does not depend on i, and the row step of i goes in the scalar offset.
+  const uint32_t pofs = (uint32_t)(((lane & 7) ^ ((4 * wave + (lane >> 4)) & 7)) * 16);
+  const uint32_t vrow = (uint32_t)(wave * 8 + (lane >> 3)) * row_bytes + pofs;
+  auto dma = [&](int slot_ofs, int op, uint32_t kofs, int i) {
+    uint32_t voff = vrow;
+    if (KTAIL && kofs + pofs >= row_bytes) voff = oob;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? rb : ra, (lds_ptr_t)(smem + slot_ofs + (wave + 4 * i) * 1024),
+                                             16, voff, kofs + (uint32_t)(32 * i) * row_bytes, 0, 0);
   };
 
   f32x16 acc[4][4];
@@ -334,14 +340,14 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ x, int T, int K, const uint16
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
   const int lrow = lane & 31, lhalf = lane >> 5;
+  const int fsw = (lrow >> 1) & 7;
   bf16x8_t a[2][4], b[2][4];
-  // fragment f (0..3: b0..b3, 4..7: a0..a3) of sub-step kk into register set c
-  auto frag = [&](int buf, int kk, int c, int f) {
+  // fragment f (0..3: b0..b3, 4..7: a0..a3) of sub-step kk (0..3) into register set c
+  auto frag = [&](int sa, int sb, int kk, int c, int f) {
     const int i = f & 3;
     const int row = (f < 4 ? wt : wn) + i * 32 + lrow;
-    const int piece = (kk * 2 + lhalf) ^ ((row >> 2) & 3);
-    const bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(smem + buf * H_STAGE + (f < 4 ? H_TILE : 0) +
-                                                          row * H_ROW + piece * 16);
+    const int piece = (2 * kk + lhalf) ^ fsw;
+    const bf16x8_t v = *reinterpret_cast<const bf16x8_t*>(smem + (f < 4 ? sb : sa) + row * Q_ROW + piece * 16);
     if (f < 4) b[c][i] = v; else a[c][i] = v;
   };
   auto mfma_row = [&](int c, int i) {
@@ -350,64 +356,85 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ x, int T, int K, const uint16
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[c][i], b[c][j], acc[i][j], 0, 0, 0);
   };
 
-  // prologue: stages 0 .. H_STAGES-2
+  // prologue: A0 -> slot 0, B0 -> slot 1, A1 -> slot 2
 #pragma unroll
-  for (int s = 0; s < H_STAGES - 1; ++s)
+  for (int i = 0; i < Q_DMA; ++i) dma(0, 0, 0u, i);
 #pragma unroll
-    for (int j = 0; j < H_DMA; ++j) dma(s, s < nk ? (uint32_t)s * H_ROW : oob, j);
-  wait_vm<(H_STAGES - 2) * H_DMA>();
+  for (int i = 0; i < Q_DMA; ++i) dma(Q_CHUNK, 1, 0u, i);
+#pragma unroll
+  for (int i = 0; i < Q_DMA; ++i) dma(2 * Q_CHUNK, 0, nk > 1 ? (uint32_t)Q_ROW : oob, i);
+  wait_vm<Q_DMA>();
   bare_barrier();
 #pragma unroll
-  for (int f = 0; f < 8; ++f) frag(0, 0, 0, f);
+  for (int f = 0; f < 8; ++f) frag(0, Q_CHUNK, 0, 0, f);
 
-  int cur = 0;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int nxt = cur + 1 == H_STAGES ? 0 : cur + 1;       // buffer of stage kt+1
-    const int pfb = cur == 0 ? H_STAGES - 1 : cur - 1;       // buffer of stage kt+3 (= kt-1's)
-    const uint32_t kofs = kt + H_STAGES - 1 < nk ? (uint32_t)(kt + H_STAGES - 1) * H_ROW : oob;
-    // sub-step 0: MFMAs on set 0; sub-step 1's fragments into set 1; DMAs 0-3
+  // Chunk c (A_d = 2d, B_d = 2d+1) lives in ring slot c % 5. While slice d
+  // is computed, B_{d+1} (slot (2d+3) % 5) and A_{d+2} (slot (2d+4) % 5) are
+  // fetched into the slots of A_{d-1} and B_{d-1}, freed by the previous
+  // slice's barrier. The slot offsets are computed per slice (an unrolled
+  // ring makes every fragment address loop-invariant: 232 spilled VGPRs).
+  int base = 0;   // (2d) % 5
+  for (int d = 0; d < nk; ++d) {
+    {
+      auto slot = [&](int m) { const int v = base + m; return (v >= Q_SLOTS ? v - Q_SLOTS : v) * Q_CHUNK; };
+      const int sa = slot(0), sb = slot(1), sa1 = slot(2), sb1 = slot(3), sa2 = slot(4);
+      const uint32_t kb1 = d + 1 < nk ? (uint32_t)(d + 1) * Q_ROW : oob;
+      const uint32_t ka2 = d + 2 < nk ? (uint32_t)(d + 2) * Q_ROW : oob;
+      // sub-step 0: MFMAs on set 0; sub-step 1's fragments into set 1; B_{d+1}, two DMAs per quarter
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      __builtin_amdgcn_sched_barrier(0);
-      dma(pfb, kofs, q);
-      frag(cur, 1, 1, 2 * q);
-      frag(cur, 1, 1, 2 * q + 1);
-      mfma_row(0, q);
-      SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1);
-      SGB(SG_MFMA, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1);
-    }
-    // sub-step 1, first quarter, then publish stage kt+1: each wave waits for
-    // its own DMAs of that stage (only the 5 issued since may still fly) and
-    // for its LDS reads of stage kt, then the barrier
-    __builtin_amdgcn_sched_barrier(0);
-    dma(pfb, kofs, 4);
-    mfma_row(1, 0);
-    SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 3);
-    __builtin_amdgcn_sched_barrier(0);
-    wait_vm<(H_STAGES - 3) * H_DMA + 5>();
-    wait_lgkm0();
-    bare_barrier();
-    // quarters 1-3: stage kt+1's sub-step-0 fragments into set 0 (3 + 3 + 2)
-#pragma unroll
-    for (int q = 1; q < 4; ++q) {
-      __builtin_amdgcn_sched_barrier(0);
-      dma(pfb, kofs, 4 + q);
-      const int f0 = q == 1 ? 0 : (q == 2 ? 3 : 6), nf = q == 3 ? 2 : 3;
-#pragma unroll
-      for (int f = 0; f < nf; ++f) frag(nxt, 0, 0, f0 + f);
-      mfma_row(1, q);
-      if (q < 3) {
+      for (int q = 0; q < 4; ++q) {
+        __builtin_amdgcn_sched_barrier(0);
+        dma(sb1, 1, kb1, 2 * q);
+        dma(sb1, 1, kb1, 2 * q + 1);
+        frag(sa, sb, 1, 1, 2 * q);
+        frag(sa, sb, 1, 1, 2 * q + 1);
+        mfma_row(0, q);
         SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1);
-        SGB(SG_DSR, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1);
-      } else {
-        SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1);
-        SGB(SG_MFMA, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1);
+        SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1);
+      }
+      // sub-steps 1 and 2: A_{d+2}, one DMA per quarter
+#pragma unroll
+      for (int kk = 1; kk < 3; ++kk) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          __builtin_amdgcn_sched_barrier(0);
+          dma(sa2, 0, ka2, (kk - 1) * 4 + q);
+          frag(sa, sb, kk + 1, (kk + 1) & 1, 2 * q);
+          frag(sa, sb, kk + 1, (kk + 1) & 1, 2 * q + 1);
+          mfma_row(kk & 1, q);
+          SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1);
+          SGB(SG_MFMA, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1);
+        }
+      }
+      // sub-step 3, first quarter, then publish slice d+1: each wave waits
+      // for its own DMAs of A_{d+1} and B_{d+1} (only A_{d+2}'s 8 may still
+      // fly) and for its LDS reads of slice d, then the barrier
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_row(1, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vm<Q_DMA>();
+      wait_lgkm0();
+      bare_barrier();
+      // quarters 1-3: slice d+1's sub-step-0 fragments into set 0 (3 + 3 + 2)
+#pragma unroll
+      for (int q = 1; q < 4; ++q) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int f0 = q == 1 ? 0 : (q == 2 ? 3 : 6), nf = q == 3 ? 2 : 3;
+#pragma unroll
+        for (int f = 0; f < nf; ++f) frag(sa1, sb1, 0, 0, f0 + f);
+        mfma_row(1, q);
+        if (q < 3) {
+          SGB(SG_MFMA, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1);
+          SGB(SG_MFMA, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1);
+        } else {
+          SGB(SG_MFMA, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 2);
+        }
       }
     }
-    cur = nxt;
+    base = base + 2 >= Q_SLOTS ? base + 2 - Q_SLOTS : base + 2;
   }
   __builtin_amdgcn_sched_barrier(0);
-  wait_vm<0>();   // the zero-fill DMAs of the last stages land before LDS is reused
+  wait_vm<0>();   // the zero-fill DMAs of the last slices land before LDS is reused
   store_tile(acc, smem, kv, T, N, t0, n0, wn, wt, lane, wave, ep);
 }
 
@@ -502,12 +529,12 @@ void gemm_mxfp8_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict
   store_tile(acc, smem, kv, T, N, t0, n0, wn, wt, lane, wave, ep);
 }
 
-// Paced MXFP8 GEMM: the bf16 kernel's pipeline on the 32x32x64 scaled MFMA.
-// A k stage is 64 e4m3 per row (64-byte LDS rows, the bf16 kernel's layout
-// and swizzle, four stages), i.e. exactly one MFMA k step, and takes the
-// same time as a bf16 stage (16 MFMAs of twice the work), so the DMA pacing
-// (stage k+3 spread over stage k, 8 DMAs per wave) and the barrier position
-// carry over. Lane (row l%32, group g = l/32) reads pieces g and 2+g of its
+// Paced MXFP8 GEMM on the 32x32x64 scaled MFMA. A k stage is 64 e4m3 per
+// row (64-byte LDS rows of 4 pieces, piece p of row r at p ^ ((r >> 2) & 3),
+// four stages), i.e. exactly one MFMA k step (16 MFMAs per wave); the DMAs
+// of stage k+3 are spread over stage k (8 per wave, one per 2 MFMAs) and the
+// barrier that publishes stage k+1 sits after the first 4 of its last 16
+// MFMAs. Lane (row l%32, group g = l/32) reads pieces g and 2+g of its
 // row (k bytes 16g.. and 32+16g..) and passes the E8M0 byte of k block
 // 2*stage + g. All of the tile's scale bytes are staged in LDS once, before
 // the first stage: W's 8 block rows and x's 256 token rows are contiguous in
@@ -700,8 +727,8 @@ void gemm_mx_paced_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restr
   store_tile(acc, smem, kv, T, N, t0, n0, wn, wt, lane, wave, ep);
 }
 
-hipError_t set_lds(const void* fn) {
-  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+hipError_t set_lds(const void* fn, int bytes = LDS_BYTES) {
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
 }  // namespace
@@ -712,13 +739,13 @@ hipError_t launch_gemm_bf16(const void* x, int64_t T, int K, const void* w, int 
   const int tiles_t = (int)((T + BN - 1) / BN);
   const dim3 grid(tiles_n * tiles_t), block(THREADS);
   hipError_t e;
-  if (K % 32 == 0) {
-    if ((e = set_lds((const void*)gemm_bf16_kernel<false>)) != hipSuccess) return e;
-    hipLaunchKernelGGL(gemm_bf16_kernel<false>, grid, block, LDS_BYTES, s, (const uint16_t*)x, (int)T, K,
+  if (K % 64 == 0) {
+    if ((e = set_lds((const void*)gemm_bf16_kernel<false>, Q_LDS)) != hipSuccess) return e;
+    hipLaunchKernelGGL(gemm_bf16_kernel<false>, grid, block, Q_LDS, s, (const uint16_t*)x, (int)T, K,
                        (const uint16_t*)w, N, (uint16_t*)kv, tiles_n, tiles_t, ep);
   } else {
-    if ((e = set_lds((const void*)gemm_bf16_kernel<true>)) != hipSuccess) return e;
-    hipLaunchKernelGGL(gemm_bf16_kernel<true>, grid, block, LDS_BYTES, s, (const uint16_t*)x, (int)T, K,
+    if ((e = set_lds((const void*)gemm_bf16_kernel<true>, Q_LDS)) != hipSuccess) return e;
+    hipLaunchKernelGGL(gemm_bf16_kernel<true>, grid, block, Q_LDS, s, (const uint16_t*)x, (int)T, K,
                        (const uint16_t*)w, N, (uint16_t*)kv, tiles_n, tiles_t, ep);
   }
   return hipGetLastError();

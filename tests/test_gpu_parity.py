@@ -332,9 +332,10 @@ def test_wkv(name):
 @pytest.mark.parametrize("fmt", ["bf16", "mxfp8"])
 @pytest.mark.parametrize("T,K,N", [(1, 256, 96), (17, 384, 288), (65, 512, 544), (300, 640, 800),
                                    (513, 1024, 320), (64, 256, 768),
-                                   # bf16 only: K % 32 != 0 (partial last k stage), N % 8 == 4
-                                   # (half 16-byte chunk at a row's end), K below one stage
-                                   (33, 264, 100), (257, 72, 260), (1, 8, 4)])
+                                   # bf16 only: K % 64 != 0 (partial last k slice), N % 8 == 4
+                                   # (half 16-byte chunk at a row's end), K below one slice
+                                   (33, 264, 100), (257, 72, 260), (1, 8, 4),
+                                   (40, 96, 264), (3, 32, 512), (130, 160, 132)])
 def test_wkv_ragged_shapes(fmt, T, K, N):
     E = _E()
     g = torch.Generator(device=DEV).manual_seed(T * 7 + K + N)
