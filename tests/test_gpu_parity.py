@@ -335,7 +335,9 @@ def test_wkv(name):
                                    # bf16 only: K % 64 != 0 (partial last k slice), N % 8 == 4
                                    # (half 16-byte chunk at a row's end), K below one slice
                                    (33, 264, 100), (257, 72, 260), (1, 8, 4),
-                                   (40, 96, 264), (3, 32, 512), (130, 160, 132)])
+                                   (40, 96, 264), (3, 32, 512), (130, 160, 132),
+                                   # one and two whole k slices
+                                   (5, 64, 256), (70, 128, 136)])
 def test_wkv_ragged_shapes(fmt, T, K, N):
     E = _E()
     g = torch.Generator(device=DEV).manual_seed(T * 7 + K + N)
