@@ -66,7 +66,7 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 constexpr int BM = 256;      // W rows per block
 constexpr int BN = 256;      // tokens per block
 constexpr int THREADS = 256;
-constexpr int LDS_BYTES = 128 * 1024;            // every variant; also the epilogue's staging tile
+constexpr int LDS_BYTES = 128 * 1024;            // MXFP8 stages; the epilogue's staging tile (bf16 ring: Q_LDS)
 // MXFP8: 128-byte k stages, two of them
 constexpr int ROW_BYTES = 128;
 constexpr int PIECES = ROW_BYTES / 16;
