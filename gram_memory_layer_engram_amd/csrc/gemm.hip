@@ -37,8 +37,8 @@
 //    publishes slice d+1 sits after the first 4 of the last 16 MFMAs of
 //    slice d, and the next slice's first fragments are read under the other
 //    12.
-//  * MXFP8 (K % 512 == 0, K <= 3584): a four-stage pipeline of 64-e4m3
-//    stages (gemm_mx_paced_kernel, described above it). Other K: a plain two-stage
+//  * MXFP8 (K % 512 == 0, K <= 3584): two buffers of 128-e4m3 slices
+//    (gemm_mx_paced_kernel, described above it). Other K: a plain two-stage
 //    kernel with 128-byte k stages (piece p of row r at p ^ ((r >> 1) & 7)).
 //  * Epilogue: the bf16 tile is staged in LDS as [token][n] (512-byte rows,
 //    16-byte chunks XOR-swizzled by token) and written back as whole rows,
@@ -72,13 +72,7 @@ constexpr int ROW_BYTES = 128;
 constexpr int PIECES = ROW_BYTES / 16;
 constexpr int TILE_BYTES = BM * ROW_BYTES;       // 32 KiB
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;      // A + B
-// paced MXFP8: 64-byte k stages, four of them
-constexpr int H_ROW = 64;
-constexpr int H_TILE = BM * H_ROW;               // 16 KiB
-constexpr int H_STAGE = 2 * H_TILE;
-constexpr int H_STAGES = 4;
-constexpr int H_DMA = 8;                         // DMA instructions per wave per stage
-static_assert(H_STAGES * H_STAGE == LDS_BYTES && 2 * STAGE_BYTES == LDS_BYTES, "LDS budget");
+static_assert(2 * STAGE_BYTES == LDS_BYTES, "LDS budget");
 static_assert(BN * 512 == LDS_BYTES, "epilogue staging tile");
 // bf16: 64-element k slices (128-byte LDS rows of 8 pieces, piece p of row
 // r at p ^ ((r >> 1) & 7)); each operand's slice is a 32 KiB chunk in a ring
@@ -530,17 +524,26 @@ void gemm_mxfp8_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict
 }
 
 // Paced MXFP8 GEMM on the 32x32x64 scaled MFMA. A k stage is 64 e4m3 per
-// row (64-byte LDS rows of 4 pieces, piece p of row r at p ^ ((r >> 2) & 3),
-// four stages), i.e. exactly one MFMA k step (16 MFMAs per wave); the DMAs
-// of stage k+3 are spread over stage k (8 per wave, one per 2 MFMAs) and the
-// barrier that publishes stage k+1 sits after the first 4 of its last 16
-// MFMAs. Lane (row l%32, group g = l/32) reads pieces g and 2+g of its
-// row (k bytes 16g.. and 32+16g..) and passes the E8M0 byte of k block
+// row, exactly one MFMA k step (16 MFMAs per wave); two stages form a slice
+// of 128-byte LDS rows, so a DMA instruction fetches 8 rows x 128 bytes, 8
+// whole cache lines (with one 64-byte stage per buffer and four buffers it
+// touched half of 16 lines: long-prefill GEMM 3491 -> 3395 us, prefill
+// shape ~400 -> ~381 us). Two slice buffers of 64 KiB: during a slice's
+// first stage the 16 DMAs of the next slice go out, four per quarter, and
+// the barrier that publishes it sits after the first 12 MFMAs of the second
+// stage (~37% of a slice of lead). Lane (row l%32, group g = l/32) reads,
+// for the slice's stage h, pieces 4h+g and 4h+2+g of its row (k bytes 16g..
+// and 32+16g.. of the stage) and passes the E8M0 byte of k block
 // 2*stage + g. All of the tile's scale bytes are staged in LDS once, before
 // the first stage: W's 8 block rows and x's 256 token rows are contiguous in
 // their [rows, K/32] arrays. Per stage: A fragments stream one row block
 // ahead (two register sets); B fragments, A row 0 and the scale bytes of the
-// next stage are read under the last 4 MFMAs, after the barrier.
+// next stage are read under the last 4 MFMAs (after the barrier when the
+// next stage opens a new slice).
+constexpr int S_ROW = 128;                      // paced MXFP8: 128-byte slices (two k steps)
+constexpr int S_TILE = BM * S_ROW;              // 32 KiB
+constexpr int S_SLICE = 2 * S_TILE;             // A + B, two slice buffers = LDS_BYTES
+static_assert(2 * S_SLICE == LDS_BYTES, "MXFP8 slice buffers");
 constexpr int MX_SCALE_A = LDS_BYTES;           // 8 W block rows x K/32 bytes (<= 1 KiB)
 constexpr int MX_SCALE_B = LDS_BYTES + 1024;    // 256 token rows x K/32 bytes
 constexpr int MX_MAX_KB = (160 * 1024 - MX_SCALE_B) / BN;
@@ -579,21 +582,19 @@ void gemm_mx_paced_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restr
                                                (uint32_t)(i * 1024 + lane * 16), 0, 0, 0);
   }
 
-  // DMA i of an operand (i = 0..3): LDS rows 16*(wave + 4i) .. +16, lane l
-  // fetching row 16*(wave+4i) + l/4, piece (l%4) ^ ((row >> 2) & 3).
-  uint32_t doff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (wave + 4 * i) * 16 + (lane >> 2);
-    doff[i] = (uint32_t)r * row_bytes + (uint32_t)(((lane & 3) ^ ((r >> 2) & 3)) * 16);
-  }
+  // A slice is two MFMA k steps (128 e4m3 per row, 128-byte LDS rows of 8
+  // pieces, piece p of row r at p ^ ((r >> 1) & 7)); two slice buffers of
+  // 64 KiB (A then B). DMA j (0..15) of a slice: operand B for j < 8, then A;
+  // i = j % 8 fills LDS rows 8*(wave + 4i) .. +8, lane l fetching row
+  // 8*(wave + 4i) + l/8, piece (l%8) ^ ((row >> 1) & 7) (independent of i).
+  const uint32_t pofs = (uint32_t)(((lane & 7) ^ ((4 * wave + (lane >> 4)) & 7)) * 16);
+  const uint32_t vrow = (uint32_t)(wave * 8 + (lane >> 3)) * row_bytes + pofs;
   auto dma = [&](int buf, uint32_t kofs, int j) {
-    const int i = j >> 1, op = j & 1;
-    const uint32_t off = kofs == oob ? oob : doff[i] + kofs;
+    const int i = j & 7, op = j < 8 ? 1 : 0;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? rb : ra,
-                                             (lds_ptr_t)(smem + buf * H_STAGE + op * H_TILE +
+                                             (lds_ptr_t)(smem + buf * S_SLICE + op * S_TILE +
                                                          (wave + 4 * i) * 1024),
-                                             16, off, 0, 0, 0);
+                                             16, vrow, kofs + (uint32_t)(32 * i) * row_bytes, 0, 0);
   };
 
   f32x16 acc[4][4];
@@ -608,11 +609,11 @@ void gemm_mx_paced_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restr
   // LDS reads as vector types: read through the 16-byte struct type, the
   // compiler could not tell them from the DMAs still writing LDS and waited
   // for every one of them (vmcnt(0)) before each read
-  auto frag = [&](int buf, int op, int row) {
-    const char* base = smem + buf * H_STAGE + op * H_TILE + row * H_ROW;
-    const int sw = (row >> 2) & 3;
-    const i32x4 lo = *reinterpret_cast<const i32x4*>(base + ((lg ^ sw) << 4));
-    const i32x4 hi = *reinterpret_cast<const i32x4*>(base + (((2 + lg) ^ sw) << 4));
+  auto frag = [&](int buf, int half, int op, int row) {
+    const char* base = smem + buf * S_SLICE + op * S_TILE + row * S_ROW;
+    const int sw = (row >> 1) & 7;
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(base + (((4 * half + lg) ^ sw) << 4));
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(base + (((4 * half + 2 + lg) ^ sw) << 4));
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
   // Scale bytes of 4 stages at a time: for its A row block (or B row) a lane
@@ -639,79 +640,94 @@ void gemm_mx_paced_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restr
                                                                  sb[j]);
   };
 
-  // prologue: stages 0 .. H_STAGES-2
+  // prologue: slice 0 into buffer 0
 #pragma unroll
-  for (int st = 0; st < H_STAGES - 1; ++st)
-#pragma unroll
-    for (int j = 0; j < H_DMA; ++j) dma(st, st < nk ? (uint32_t)st * H_ROW : oob, j);
-  wait_vm<(H_STAGES - 2) * H_DMA>();
+  for (int j = 0; j < 16; ++j) dma(0, 0u, j);
+  wait_vm<0>();
   bare_barrier();
   u32x2 sa8[4], sb8[4];
   scales8(0, sa8, sb8);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) b[j] = frag(0, 1, wt + j * 32 + lrow);
-  a0 = frag(0, 0, wn + lrow);
+  for (int j = 0; j < 4; ++j) b[j] = frag(0, 0, 1, wt + j * 32 + lrow);
+  a0 = frag(0, 0, 0, wn + lrow);
 
-  // nk % 4 == 0 (K % 512 == 0): groups of four stages, one per LDS buffer,
-  // so every buffer index below is a constant
+  // nk % 4 == 0 (K % 512 == 0): groups of four stages = two slices, so
+  // every buffer index below is a constant. Stage kt is half kt % 2 of slice
+  // kt / 2; in a slice's first half the 16 DMAs of the next slice go out
+  // (four per quarter, into the other buffer, free since the last barrier),
+  // and the barrier that publishes it sits in the second half.
   for (int kt4 = 0; kt4 < nk; kt4 += 4) {
     u32x2 na8[4], nb8[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int kt = kt4 + u;
-      const int cur = u, nxt = (u + 1) & 3, pfb = (u + 3) & 3;   // buffers of stages kt, kt+1, kt+3
-      const uint32_t kofs = kt + H_STAGES - 1 < nk ? (uint32_t)(kt + H_STAGES - 1) * H_ROW : oob;
+      const int half = u & 1, cur = u >> 1;
+      const int nbuf = half ? cur ^ 1 : cur, nhalf = half ^ 1;   // buffer and half of stage kt+1
+      const uint32_t kofs = (kt >> 1) + 1 < nk / 2 ? (uint32_t)((kt >> 1) + 1) * S_ROW : oob;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         sa[i] = pick(sa8[i], u);
         sb[i] = pick(sb8[i], u);
       }
-      // quarters 0, 1: two DMAs, the next A row block, 4 MFMAs
+      // quarters 0, 1: the next A row blocks, 4 MFMAs each (first half: 4 DMAs each)
       __builtin_amdgcn_sched_barrier(0);
-      dma(pfb, kofs, 0);
-      dma(pfb, kofs, 1);
-      a1 = frag(cur, 0, wn + 32 + lrow);
+      if (!half) { dma(cur ^ 1, kofs, 0); dma(cur ^ 1, kofs, 1); dma(cur ^ 1, kofs, 2); dma(cur ^ 1, kofs, 3); }
+      a1 = frag(cur, half, 0, wn + 32 + lrow);
       mfma_row(a0, 0);
-      SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1);
-      SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1);
+      if (!half) {
+        SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 1);
+        SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1);
+      } else {
+        SGB(SG_MFMA, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 2);
+      }
       __builtin_amdgcn_sched_barrier(0);
-      dma(pfb, kofs, 2);
-      dma(pfb, kofs, 3);
-      a0 = frag(cur, 0, wn + 64 + lrow);
+      if (!half) { dma(cur ^ 1, kofs, 4); dma(cur ^ 1, kofs, 5); dma(cur ^ 1, kofs, 6); dma(cur ^ 1, kofs, 7); }
+      a0 = frag(cur, half, 0, wn + 64 + lrow);
       mfma_row(a1, 1);
-      SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1);
-      SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1);
-      // quarter 2: the last reads of this stage, then publish stage kt+1: each
-      // wave waits for its own DMAs of that stage (only the 5 issued since may
-      // still fly) and for its LDS reads, then the barrier
+      if (!half) {
+        SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 1);
+        SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1);
+      } else {
+        SGB(SG_MFMA, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 2);
+      }
+      // quarter 2: the last A row block of this stage; in a second half, then
+      // publish the next slice: each wave waits for all of its DMAs and its
+      // LDS reads, then the barrier
       __builtin_amdgcn_sched_barrier(0);
-      dma(pfb, kofs, 4);
-      a1 = frag(cur, 0, wn + 96 + lrow);
+      if (!half) { dma(cur ^ 1, kofs, 8); dma(cur ^ 1, kofs, 9); dma(cur ^ 1, kofs, 10); dma(cur ^ 1, kofs, 11); }
+      a1 = frag(cur, half, 0, wn + 96 + lrow);
       mfma_row(a0, 2);
-      SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1);
-      SGB(SG_MFMA, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1);
+      if (!half) {
+        SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 1);
+        SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1);
+      } else {
+        SGB(SG_MFMA, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 2);
+      }
       __builtin_amdgcn_sched_barrier(0);
-      wait_vm<(H_STAGES - 3) * H_DMA + 5>();
-      wait_lgkm0();
-      bare_barrier();
+      if (half) {
+        wait_vm<0>();
+        wait_lgkm0();
+        bare_barrier();
+      }
       // quarter 3: stage kt+1's B fragments and A row block 0 (and, closing a
       // group, the next group's scale bytes) under the last 4 MFMAs
       __builtin_amdgcn_sched_barrier(0);
-      dma(pfb, kofs, 5);
-      dma(pfb, kofs, 6);
-      dma(pfb, kofs, 7);
+      if (!half) { dma(cur ^ 1, kofs, 12); dma(cur ^ 1, kofs, 13); dma(cur ^ 1, kofs, 14); dma(cur ^ 1, kofs, 15); }
       i32x8 nb[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) nb[j] = frag(nxt, 1, wt + j * 32 + lrow);
-      a0 = frag(nxt, 0, wn + lrow);
+      for (int j = 0; j < 4; ++j) nb[j] = frag(nbuf, nhalf, 1, wt + j * 32 + lrow);
+      a0 = frag(nbuf, nhalf, 0, wn + lrow);
       if (u == 3) scales8(min(kt4 + 4, nk - 4), na8, nb8);   // the last group reloads itself, unused
       mfma_row(a1, 3);
       if (u == 3) {
-        SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 5); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1);
-        SGB(SG_DSR, 5); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 4); SGB(SG_MFMA, 1); SGB(SG_DSR, 4);
-      } else {
+        SGB(SG_MFMA, 1); SGB(SG_DSR, 6); SGB(SG_MFMA, 1); SGB(SG_DSR, 6); SGB(SG_MFMA, 1); SGB(SG_DSR, 6);
+        SGB(SG_MFMA, 1);
+      } else if (!half) {
         SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 4); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1);
-        SGB(SG_DSR, 3); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 3); SGB(SG_MFMA, 1);
+        SGB(SG_DSR, 3); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 3); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1);
+      } else {
+        SGB(SG_MFMA, 1); SGB(SG_DSR, 4); SGB(SG_MFMA, 1); SGB(SG_DSR, 3); SGB(SG_MFMA, 1); SGB(SG_DSR, 3);
+        SGB(SG_MFMA, 1);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) b[j] = nb[j];
