@@ -349,7 +349,18 @@ def test_wkv_ragged_shapes(fmt, T, K, N):
         _kv_checks(bits(kv), ref_bits, ref64, strict=True)
     else:
         if K % 128 or N % 32:
-            pytest.skip("MXFP8 needs K % 128 == 0 and N % 32 == 0")
+            # the MXFP8 kernels need K % 128 == 0 and N % 32 == 0: the C ABI
+            # refuses other shapes before any launch and leaves kv untouched
+            L = E.load_library()
+            w = torch.zeros((N, K), dtype=torch.uint8, device=DEV)
+            ws = torch.full((max(1, N // 32), max(1, K // 32)), 127, dtype=torch.uint8, device=DEV)
+            kv = torch.full((T, N), 7, dtype=torch.int16, device=DEV)
+            st = L.engram_wkv(x.data_ptr(), T, K, w.data_ptr(), ws.data_ptr(), E.W_MXFP8, N, kv.data_ptr(),
+                              None, 0, torch.cuda.current_stream().cuda_stream)
+            torch.cuda.synchronize()
+            assert st == E.ENGRAM_EUNSUPPORTED
+            assert bool((kv == 7).all())
+            return
         w = torch.randn((N, K), generator=g, device=DEV).to(torch.float8_e4m3fn).view(torch.uint8)
         ws = (127 + torch.randint(-8, 1, (N // 32, K // 32), generator=g, device=DEV)).to(torch.uint8)
         kv = E.wkv(x, w, ws)
@@ -872,3 +883,54 @@ def test_argument_errors():
     # operand shapes that disagree are refused by the binding
     with pytest.raises(ValueError):
         E.wkv(torch.zeros((4, 64), dtype=torch.bfloat16, device=DEV), inp["w"])
+
+
+@pytest.mark.parametrize("route", ["gate", "epilogue", "store_kv", "decode_gemv"])
+def test_gate_sign_symmetry_range_and_mask(route):
+    """What the gate's definition fixes whatever the data, on each route that
+    forms the gate (the plain gate kernel on a given kv, the bf16 forward
+    with the GEMM's gate epilogue and with kv stored, the MXFP8 decode
+    forward): negating the hidden stream negates every product of the dot
+    and leaves the square sums alone, so the normalized dot and its signed
+    square root flip sign exactly and the gate becomes 1 - g; active gates
+    lie strictly inside (0, 1) and at least the clamp's sigma(1e-3) - 1/2
+    away from 1/2; masked rows get gate 0 and their hidden bits."""
+    E = _E()
+    g = torch.Generator(device=DEV).manual_seed(4242 + 17 * len(route))
+    T, dim, hc = (16, 256, 2) if route == "decode_gemv" else (300, 512, 2)
+    R, C, hd = 2503, 4, 128
+    K, N = C * hd, (hc + 1) * dim
+    hidden = torch.randn((T, hc, dim), generator=g, device=DEV).to(torch.bfloat16)
+    sign = torch.tensor(-32768, dtype=torch.int16, device=DEV)
+    neg = (hidden.view(torch.int16) ^ sign).view(torch.bfloat16)
+    q = (1 + 0.1 * torch.randn((hc, dim), generator=g, device=DEV)).to(torch.bfloat16)
+    k = (1 + 0.1 * torch.randn((hc, dim), generator=g, device=DEV)).to(torch.bfloat16)
+    mask = torch.rand((T,), generator=g, device=DEV) > 0.2
+    kv = (torch.randn((T, N), generator=g, device=DEV) * 0.5).to(torch.bfloat16)
+    table = (torch.randn((R, hd), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    ids = torch.randint(0, R, (T, C), generator=g, device=DEV, dtype=torch.int32)
+    if route == "decode_gemv":
+        w = torch.randn((N, K), generator=g, device=DEV).to(torch.float8_e4m3fn).view(torch.uint8)
+        ws = (127 + torch.randint(-8, 1, (N // 32, K // 32), generator=g, device=DEV)).to(torch.uint8)
+    else:
+        w = (torch.randn((N, K), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+        ws = None
+    _say(f"gate symmetry route={route} T={T} dim={dim} hc={hc}")
+    res = []
+    for h in (hidden, neg):
+        gate_out = torch.empty((T, hc), dtype=torch.float32, device=DEV)
+        if route == "gate":
+            out = E.gate(h, kv, q, k, mask, 1e-6, 1e-6, gate_out=gate_out)
+        else:
+            out = E.forward(table, ids, w, ws, h, q, k, mask, gate_out=gate_out, store_kv=route == "store_kv")
+        torch.cuda.synchronize()
+        res.append((bits(out), gate_out.cpu().numpy(), bits(h)))
+    m = mask.cpu().numpy()
+    (o_p, g_p, h_p), (o_n, g_n, h_n) = res
+    for o_, g_, h_ in res:
+        act = g_[m]
+        assert np.all((act > 0) & (act < 1))
+        assert np.all(np.abs(act - 0.5) >= 0.5 / (1 + np.exp(-1e-3)) - 0.5 - 1e-6)
+        assert np.all(g_[~m] == 0)
+        assert np.array_equal(o_[~m], h_[~m])
+    assert np.max(np.abs(g_n[m] - (1 - g_p[m]))) <= 1e-5
