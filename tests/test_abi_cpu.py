@@ -8,6 +8,7 @@ import ctypes
 import os
 import re
 import subprocess
+import sys
 import tempfile
 
 import numpy as np
@@ -216,3 +217,13 @@ def test_binding_has_no_cpu_fallback(tmp_path):
     ids = torch.zeros((2, 3), dtype=torch.int32)
     with pytest.raises(ValueError, match="device tensors"):
         engram.lookup(table, ids, rows_out=torch.empty((2, 3, 32), dtype=torch.bfloat16))
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """bench.py measures one GPU; asked for more it exits with status 2 and
+    says why, before touching any device."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in (r.stdout + r.stderr)
