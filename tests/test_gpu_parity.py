@@ -934,3 +934,40 @@ def test_gate_sign_symmetry_range_and_mask(route):
         assert np.all(g_[~m] == 0)
         assert np.array_equal(o_[~m], h_[~m])
     assert np.max(np.abs(g_n[m] - (1 - g_p[m]))) <= 1e-5
+
+
+@pytest.mark.parametrize("route,T", [("bf16", 300), ("mxfp8_gemv", 16), ("mxfp8_gemm", 257), ("single_launch", 16)])
+def test_forward_strided_hash_ids(route, T):
+    """engram_forward reads hash_ids through their strides on every route: a
+    layer's view of a [T, layers, C] hash tensor (row stride 3*C) and a
+    column-major view (column stride T) give the same bits as contiguous ids
+    (the bf16 lookup, the fused gather + MX quantize before the decode GEMV
+    and before the scaled GEMM, and the single launch)."""
+    E = _E()
+    hc, dim = 2, 256
+    c = _decode_case(T, dim, hc, seed=9100 + T + len(route))
+    if route == "bf16":
+        g = torch.Generator(device=DEV).manual_seed(9200 + T)
+        K, N = c["ids"].shape[1] * c["table"].shape[1], (hc + 1) * dim
+        c["w"] = (torch.randn((N, K), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+        c["ws"] = None
+    ids = c["ids"]
+    C = ids.shape[1]
+    layers = torch.randint(0, c["table"].shape[0], (T, 3, C), device=DEV, dtype=torch.int32)
+    layers[:, 1, :] = ids
+    layer_view = layers[:, 1, :]
+    col_major = ids.t().contiguous().t()
+    assert layer_view.stride() == (3 * C, 1) and col_major.stride() == (1, T)
+    _say(f"forward strided ids route={route} T={T}")
+    outs = []
+    for v in (ids, layer_view, col_major):
+        out = E.forward(c["table"], v, c["w"], c["ws"], c["hidden"], c["q"], c["k"], c["mask"],
+                        single_launch=route == "single_launch")
+        torch.cuda.synchronize()
+        outs.append(bits(out))
+    assert np.array_equal(outs[0], outs[1])
+    assert np.array_equal(outs[0], outs[2])
+    ref = o.forward(bits(c["table"]), ids.cpu().numpy(), bits(c["w"]) if c["ws"] is None else u8(c["w"]),
+                    None if c["ws"] is None else u8(c["ws"]), bits(c["hidden"]), bits(c["q"]), bits(c["k"]),
+                    c["mask"].cpu().numpy(), 1e-6, 1e-6)
+    assert_close(bf16_values(outs[0]), bf16_values(ref["out"]), *OUT_TOL, what="out")
