@@ -416,7 +416,8 @@ def test_gate_on_shared_kv(name):
     assert np.all((act > 0) & (act < 1))
 
 
-@pytest.mark.parametrize("hc,dim", [(1, 8), (2, 256), (3, 520), (4, 2048), (4, 7168), (8, 1024), (2, 16384)])
+@pytest.mark.parametrize("hc,dim", [(1, 8), (2, 256), (3, 520), (4, 2048), (4, 7168), (8, 1024), (2, 16384),
+                                    (5, 2048), (5, 512), (6, 1024), (7, 264)])
 @pytest.mark.parametrize("T", [1, 2, 15, 65, 300])
 def test_gate_shapes(hc, dim, T):
     """Small T splits the copies over workgroups, T = 300 keeps a token's
@@ -602,6 +603,7 @@ def test_forward_small_hidden_engram_term_dominates():
 
 
 @pytest.mark.parametrize("wfmt,T,dim,hc", [("bf16", 300, 512, 3), ("bf16", 300, 136, 2), ("bf16", 1, 256, 1),
+                                           ("bf16", 300, 512, 5), ("mxfp8", 257, 256, 7), ("bf16", 130, 256, 6),
                                            ("bf16", 300, 1024, 2), ("mxfp8", 257, 1024, 3),
                                            ("mxfp8", 257, 512, 2), ("mxfp8", 200, 160, 2)])
 def test_forward_gate_epilogue_and_plain_paths(wfmt, T, dim, hc):
