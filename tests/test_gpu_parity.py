@@ -973,3 +973,25 @@ def test_forward_strided_hash_ids(route, T):
                     None if c["ws"] is None else u8(c["ws"]), bits(c["hidden"]), bits(c["q"]), bits(c["k"]),
                     c["mask"].cpu().numpy(), 1e-6, 1e-6)
     assert_close(bf16_values(outs[0]), bf16_values(ref["out"]), *OUT_TOL, what="out")
+
+
+@pytest.mark.parametrize("K", [1024, 2176, 3072, 4096, 4224])
+@pytest.mark.parametrize("T", [3, 40])
+def test_wkv_mxfp8_decode_gemv_k_range(T, K):
+    """The decode GEMV's k split at every size it takes: 1, 3 (K 2176: 17
+    k-steps over 8 waves, the last waves without any) and 4 k-steps per wave
+    (K 3072, 4096); K 4224 is past its register budget and runs the scaled
+    GEMM instead. Against the oracle's MXFP8 projection."""
+    E = _E()
+    g = torch.Generator(device=DEV).manual_seed(5100 + T + K)
+    N = 160
+    x = (torch.randn((T, K), generator=g, device=DEV) * 0.5).to(torch.bfloat16)
+    w = torch.randn((N, K), generator=g, device=DEV).to(torch.float8_e4m3fn).view(torch.uint8)
+    ws = (127 + torch.randint(-8, 1, (N // 32, K // 32), generator=g, device=DEV)).to(torch.uint8)
+    _say(f"wkv mxfp8 gemv T={T} K={K}")
+    kv = E.wkv(x, w, ws)
+    kv2 = E.wkv(x, w, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(kv.view(torch.int16), kv2.view(torch.int16))
+    ref_bits, ref64 = o.wkv(bits(x), u8(w), u8(ws))
+    _kv_checks(bits(kv), ref_bits, ref64, strict=False)
