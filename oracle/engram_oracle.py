@@ -171,7 +171,13 @@ def mx_quantize(x_bits):
       emax_elem = 8 for E4M3;
     * scale byte = X + 127, clamped to the E8M0 range [0, 254];
     * element code = e4m3fn(x / 2**(byte-127)), nearest-even, saturating;
-    * an all-zero block gets byte 0 and zero codes.
+    * an all-zero block gets byte 0 and zero codes;
+    * a block holding an infinity or a NaN has no finite maximum, so no
+      shared exponent: it gets the E8M0 NaN byte 255 and every code is the
+      e4m3fn NaN 0x7F. A NaN scale makes every element of its block NaN in
+      the MX format, so the block decodes to NaN whatever a reader does with
+      the codes (reading taken; neither the pages nor the conversion rule
+      give a finite encoding for such a block).
 
     floor(log2 a) is read from the binary exponent of a (exact, no log call).
     """
@@ -179,13 +185,16 @@ def mx_quantize(x_bits):
     T, K = x.shape
     assert K % MX_BLOCK == 0
     blocks = x.reshape(T, K // MX_BLOCK, MX_BLOCK)
-    amax = np.abs(blocks).max(axis=2)
+    finite = np.isfinite(blocks).all(axis=2)
+    amax = np.abs(np.where(np.isfinite(blocks), blocks, 0.0)).max(axis=2)
     _, e = np.frexp(amax)  # amax = f * 2**e, 0.5 <= f < 1 -> floor(log2) = e-1
     shared = (e - 1) - E4M3_EMAX
     scale_byte = np.clip(shared + 127, 0, 254)
-    scale_byte = np.where(amax == 0, 0, scale_byte).astype(np.uint8)
-    scaled = blocks / e8m0_decode(scale_byte)[:, :, None]
-    codes = e4m3fn_encode(scaled).reshape(T, K)
+    scale_byte = np.where(amax == 0, 0, scale_byte)
+    scale_byte = np.where(finite, scale_byte, 255).astype(np.uint8)
+    scaled = np.where(finite[:, :, None], blocks, 0.0) / e8m0_decode(scale_byte)[:, :, None]
+    codes = e4m3fn_encode(scaled)  # a NaN scale gives NaN quotients -> 0x7F
+    codes = np.where(finite[:, :, None], codes, np.uint8(0x7F)).reshape(T, K)
     return codes, scale_byte
 
 

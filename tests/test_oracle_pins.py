@@ -170,6 +170,40 @@ def test_mx_quantize_error_bound_and_idempotence():
     assert np.array_equal(codes2, codes) and np.array_equal(sb2, sb)
 
 
+def test_mx_quantize_non_finite_blocks_become_nan_blocks():
+    """A block holding +inf, -inf or a NaN (any payload, either sign) is the
+    E8M0 NaN scale 255 with every code 0x7F, the e4m3fn NaN; blocks of the
+    same token without one are quantized as if it were not there (here the
+    worked values of the rule: amax 1 -> byte 119, code 0x78), and the
+    dequantized non-finite block is NaN throughout."""
+    K = 32 * 4
+    bits = np.zeros((3, K), np.uint16)
+    bits[0, 5] = 0x7F80            # +inf
+    bits[0, 6] = 0x3F80            # 1.0 beside it: still a NaN block
+    bits[1, 40] = 0xFF80           # -inf in block 1
+    bits[2, 127] = 0xFFC1          # a negative NaN with a payload, in block 3
+    bits[2, 126] = 0x7FC0
+    for t in range(3):
+        fin = [b for b in range(4) if not ((t, b) in [(0, 0), (1, 1), (2, 3)])]
+        for b in fin:
+            bits[t, 32 * b] = 0x3F80                  # 1.0
+            bits[t, 32 * b + 1] = 0xBF00              # -0.5
+    codes, sb = o.mx_quantize(bits)
+    nan_blocks = [(0, 0), (1, 1), (2, 3)]
+    for t in range(3):
+        for b in range(4):
+            blk = codes[t, 32 * b:32 * b + 32]
+            if (t, b) in nan_blocks:
+                assert sb[t, b] == 255
+                assert np.all(blk == 0x7F)
+            else:
+                assert sb[t, b] == 119
+                assert blk[0] == 0x78 and blk[1] == 0xF0 and not blk[2:].any()
+    deq = o.mx_dequantize_activations(codes, sb)
+    assert np.all(np.isnan(deq[0, 0:32])) and np.all(np.isnan(deq[2, 96:128]))
+    assert deq[0, 32] == 1.0 and deq[0, 33] == -0.5
+
+
 # --------------------------------------------------------------- gather ----
 
 
