@@ -240,7 +240,7 @@ int engram_gate(const void* hidden, const void* kv, const void* q_weight,
 // scratch, whichever is larger.
 constexpr size_t kSyncBytes = kDecodeSyncBytes;
 
-bool use_decode_path(const engram_forward_args* a, int32_t K, int32_t N) {
+static bool use_decode_path(const engram_forward_args* a, int32_t K, int32_t N) {
   return a->w_format == ENGRAM_W_MXFP8 && decode_forward_supported(a->T, K, N, a->head_dim, a->dim, a->hc);
 }
 
@@ -256,9 +256,9 @@ size_t engram_forward_workspace_size(const engram_forward_args* a) {
   return kSyncBytes + bytes;
 }
 
-// Shared argument checks of the two forward entry points; sets K and N.
-int check_forward(const engram_forward_args* a, void* workspace, size_t workspace_bytes, int32_t* K,
-                  int32_t* N) {
+// Argument checks shared by the forward entry points, the workspace left
+// out; sets K and N.
+static int check_forward_args(const engram_forward_args* a, int32_t* K, int32_t* N) {
   if (!a || (a->options & ~ENGRAM_FORWARD_STORE_KV)) return ENGRAM_EINVAL;
   const int64_t K64 = (int64_t)a->n_cols * a->head_dim;
   const int64_t N64 = (int64_t)(a->hc + 1) * a->dim;
@@ -273,22 +273,24 @@ int check_forward(const engram_forward_args* a, void* workspace, size_t workspac
   if (st != ENGRAM_OK) return st;
   st = check_gate(a->hidden, (void*)16, a->q_weight, a->k_weight, a->T, a->hc, a->dim, a->out);
   if (st != ENGRAM_OK) return st;
-  st = check_wkv((void*)16, a->T, *K, a->w, a->w_scales, a->w_format, *N, (void*)16);
-  if (st != ENGRAM_OK) return st;
-  if (a->T == 0) return ENGRAM_OK;
+  return check_wkv((void*)16, a->T, *K, a->w, a->w_scales, a->w_format, *N, (void*)16);
+}
+
+// The forward entry points' checks, the caller's workspace included.
+static int check_forward(const engram_forward_args* a, void* workspace, size_t workspace_bytes, int32_t* K,
+                  int32_t* N) {
+  int st = check_forward_args(a, K, N);
+  if (st != ENGRAM_OK || a->T == 0) return st;
   const size_t need = engram_forward_workspace_size(a);
   if (!workspace || workspace_bytes < need || ((uintptr_t)workspace % kAlign)) return ENGRAM_EINVAL;
   return ENGRAM_OK;
 }
 
-int engram_forward(const engram_forward_args* a, void* workspace,
-                   size_t workspace_bytes, void* stream) {
-  int32_t K = 0, N = 0;
-  int st = check_forward(a, workspace, workspace_bytes, &K, &N);
-  if (st != ENGRAM_OK || a->T == 0) return st;
-
-  hipStream_t s = (hipStream_t)stream;
-  uint8_t* ws = (uint8_t*)workspace + kSyncBytes;
+// engram_forward's launches, given checked arguments and the workspace past
+// its flag area (rows | kv | MXFP8 staging; nothing in it needs to start at
+// zero: every byte a kernel reads was written earlier in the same call).
+static int run_forward(const engram_forward_args* a, int32_t K, int32_t N, uint8_t* ws, hipStream_t s) {
+  int st = ENGRAM_OK;
   void* rows = ws;
   void* kv = ws + round_up((size_t)a->T * K * 2);
   void* mx = (uint8_t*)kv + round_up((size_t)a->T * N * 2);
@@ -329,6 +331,14 @@ int engram_forward(const engram_forward_args* a, void* workspace,
           : launch_gate(a->hidden, kv, a->q_weight, a->k_weight, a->token_mask, a->T, a->hc,
                         a->dim, a->eps, a->clamp, a->out, a->gate_out, s);
   return hip_status(e);
+}
+
+int engram_forward(const engram_forward_args* a, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  int32_t K = 0, N = 0;
+  int st = check_forward(a, workspace, workspace_bytes, &K, &N);
+  if (st != ENGRAM_OK || a->T == 0) return st;
+  return run_forward(a, K, N, (uint8_t*)workspace + kSyncBytes, (hipStream_t)stream);
 }
 
 int engram_forward_single_launch(const engram_forward_args* a, void* workspace,

@@ -23,7 +23,10 @@
 //    descriptor's range check returns zeros past the last row of W or x, so
 //    ragged tiles need no branches; a stage that does not exist is loaded
 //    from an offset past the range (zeros into a buffer nobody reads), which
-//    keeps the loop free of branches.
+//    keeps the loop free of branches. The range check covers the vector
+//    offset only, so every DMA offset (row, k slice, piece) is carried in it
+//    and the scalar offset is 0 (gemm_dma.h; a host model of those offsets
+//    checks each against the range).
 //  * bf16: a k slice is 64 elements, so one DMA instruction fetches 8 rows x
 //    128 bytes, 8 whole cache lines (with 32-element stages it touched half
 //    of 16 lines: 627 -> 564 us for the prefill GEMM, same instructions,
@@ -54,6 +57,7 @@
 //    the hardware). Each lane therefore reads pieces 4s+g and 4s+2+g of the
 //    stage for sub-step s and passes byte 2s+g of the stage's 4 scale bytes.
 #include "common.h"
+#include "gemm_dma.h"
 
 namespace engram {
 
@@ -313,16 +317,13 @@ void gemm_bf16_kernel(const uint16_t* __restrict__ x, int T, int K, const uint16
   const uint32_t oob = (uint32_t)BM * row_bytes;   // at or past both ranges
   const int nk = (K + 63) / 64;
 
-  // DMA i (0..7) of a chunk: LDS rows 8*(wave + 4i) .. +8, lane l fetching
-  // row 8*(wave + 4i) + l/8, piece (l%8) ^ ((row >> 1) & 7); that swizzle
-  // does not depend on i, and the row step of i goes in the scalar offset.
-  const uint32_t pofs = (uint32_t)(((lane & 7) ^ ((4 * wave + (lane >> 4)) & 7)) * 16);
-  const uint32_t vrow = (uint32_t)(wave * 8 + (lane >> 3)) * row_bytes + pofs;
+  // DMA i (0..7) of a chunk: LDS rows 8*(wave + 4i) .. +8 (gemm_dma.h). The
+  // whole offset, row step and k offset included, is the range-checked
+  // vector offset; the scalar offset stays 0.
+  const dma::Lane dl = dma::lane_of(wave, lane, row_bytes);
   auto dma = [&](int slot_ofs, int op, uint32_t kofs, int i) {
-    uint32_t voff = vrow;
-    if (KTAIL && kofs + pofs >= row_bytes) voff = oob;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? rb : ra, (lds_ptr_t)(smem + slot_ofs + (wave + 4 * i) * 1024),
-                                             16, voff, kofs + (uint32_t)(32 * i) * row_bytes, 0, 0);
+                                             16, dma::voffset(dl, i, kofs, row_bytes, oob, KTAIL), 0, 0, 0);
   };
 
   f32x16 acc[4][4];
@@ -585,16 +586,15 @@ void gemm_mx_paced_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restr
   // A slice is two MFMA k steps (128 e4m3 per row, 128-byte LDS rows of 8
   // pieces, piece p of row r at p ^ ((r >> 1) & 7)); two slice buffers of
   // 64 KiB (A then B). DMA j (0..15) of a slice: operand B for j < 8, then A;
-  // i = j % 8 fills LDS rows 8*(wave + 4i) .. +8, lane l fetching row
-  // 8*(wave + 4i) + l/8, piece (l%8) ^ ((row >> 1) & 7) (independent of i).
-  const uint32_t pofs = (uint32_t)(((lane & 7) ^ ((4 * wave + (lane >> 4)) & 7)) * 16);
-  const uint32_t vrow = (uint32_t)(wave * 8 + (lane >> 3)) * row_bytes + pofs;
+  // i = j % 8 fills LDS rows 8*(wave + 4i) .. +8 (gemm_dma.h), the whole
+  // offset in the range-checked vector offset.
+  const dma::Lane dl = dma::lane_of(wave, lane, row_bytes);
   auto dma = [&](int buf, uint32_t kofs, int j) {
     const int i = j & 7, op = j < 8 ? 1 : 0;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? rb : ra,
                                              (lds_ptr_t)(smem + buf * S_SLICE + op * S_TILE +
                                                          (wave + 4 * i) * 1024),
-                                             16, vrow, kofs + (uint32_t)(32 * i) * row_bytes, 0, 0);
+                                             16, dma::voffset(dl, i, kofs, row_bytes, oob, false), 0, 0, 0);
   };
 
   f32x16 acc[4][4];

@@ -29,12 +29,21 @@ __device__ __forceinline__ int bf16_floor_log2(uint32_t mag) {
 }
 
 // Quantize one 32-element block (16 words of bf16 pairs) -> 8 code words + scale byte.
+// A block holding an infinity or a NaN gets scale byte 255 (the E8M0 NaN)
+// and every code 0x7F (the e4m3fn NaN).
 __device__ __forceinline__ int mx_block(const uint32_t* w, uint32_t* packed) {
   uint32_t amax = 0;  // bf16 magnitudes order like unsigned integers
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     amax = max(amax, w[i] & 0x7fffu);
     amax = max(amax, (w[i] >> 16) & 0x7fffu);
+  }
+  if (amax >= 0x7f80u) {
+    // an infinity or a NaN in the block: no finite shared exponent; the block
+    // becomes the E8M0 NaN scale with e4m3fn NaN codes (decodes to NaN)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) packed[i] = 0x7f7f7f7fu;
+    return 255;
   }
   int byte = 0;
   if (amax != 0) {

@@ -10,6 +10,9 @@
 //   byte   = clamp(X + 127, 0, 254); 0 for an all-zero block
 //   code   = e4m3fn(x * 2^(127 - byte)), nearest-even, saturating at 448,
 //            sign bit kept
+// A block holding an infinity or a NaN has no finite maximum: it is given
+// the E8M0 NaN scale (byte 255) and the e4m3fn NaN code 0x7F everywhere, so
+// it decodes to NaN (an MX NaN scale makes its whole block NaN).
 // The gather can be fused in front (gather_quantize_kernel): the bf16 staged
 // rows then never reach HBM. All of it is integer work on the bf16 bit patterns plus one exact
 // power-of-two multiply, so codes are reproducible bit for bit.

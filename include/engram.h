@@ -106,7 +106,9 @@ int engram_lookup_fp8(const void* table_codes, const uint8_t* table_scales,
  *   pages) is the OCP MX v1.0 conversion: per token and 32-element K block,
  *   X = floor(log2(max|x|)) - 8, scale byte = clamp(X + 127, 0, 254) (0 for an
  *   all-zero block), code = e4m3fn(x / 2^(byte-127)) round-to-nearest-even,
- *   saturating at +-448, sign kept.
+ *   saturating at +-448, sign kept. A block holding an infinity or a NaN gets
+ *   scale byte 255 (the E8M0 NaN) and every code 0x7F (the e4m3fn NaN), so
+ *   it decodes to NaN.
  *
  *   x   bf16 [T, K];  xq  uint8 e4m3fn codes [T, K];  xs  uint8 E8M0 [T, K/32].
  *   K   multiple of 32.

@@ -44,10 +44,19 @@ def ulp_distance_bf16(a_bits: np.ndarray, b_bits: np.ndarray) -> np.ndarray:
     return np.abs(ordered(a_bits) - ordered(b_bits))
 
 
-def sample_tokens(T: int, n: int, seed: int = 0) -> np.ndarray:
-    """A seeded sorted sample of token indices that always includes both ends."""
+def sample_tokens(T: int, n: int, seed: int = 0, tile: int = 256) -> np.ndarray:
+    """A seeded sorted sample of token indices: both ends, one token from
+    every ``tile``-token tile (so every token tile of a tiled kernel has a
+    checked output, the ragged last one included), then random others up to
+    ``n`` in all (more when there are more tiles than that)."""
     if T <= n:
         return np.arange(T)
     rng = np.random.default_rng(seed)
-    s = rng.choice(np.arange(1, T - 1), size=n - 2, replace=False)
-    return np.sort(np.concatenate([[0, T - 1], s]))
+    starts = np.arange(0, T, tile)
+    per_tile = starts + rng.integers(0, np.minimum(tile, T - starts))
+    chosen = np.unique(np.concatenate([[0, T - 1], per_tile]))
+    rest = np.setdiff1d(np.arange(T), chosen)
+    extra = max(0, n - len(chosen))
+    if extra:
+        chosen = np.concatenate([chosen, rng.choice(rest, size=extra, replace=False)])
+    return np.sort(chosen)
