@@ -2,6 +2,7 @@
 // Every entry point only enqueues work on the caller's stream.
 #include "../../include/engram.h"
 #include <algorithm>
+#include <mutex>
 
 #include "common.h"
 
@@ -145,6 +146,7 @@ const char* engram_status_string(int status) {
     case ENGRAM_EINVAL: return "invalid argument";
     case ENGRAM_EUNSUPPORTED: return "unsupported shape";
     case ENGRAM_EHIP: return "HIP runtime error";
+    case ENGRAM_ENOSPACE: return "input larger than the fixed scratch buffer";
     default: return "unknown status";
   }
 }
@@ -339,6 +341,50 @@ int engram_forward(const engram_forward_args* a, void* workspace,
   int st = check_forward(a, workspace, workspace_bytes, &K, &N);
   if (st != ENGRAM_OK || a->T == 0) return st;
   return run_forward(a, K, N, (uint8_t*)workspace + kSyncBytes, (hipStream_t)stream);
+}
+
+// ---- engram_forward_noalloc: engram_forward on a fixed device buffer ----
+//
+// `scratch` is a fixed buffer in device memory (one per GPU the library runs
+// on, held until the process ends). Host code never passes its name to a
+// kernel: on the host that name is only a stand-in, not a device address.
+// The device address is looked up once per device, with that device
+// current, and kept; launches take that pointer.
+
+static __device__ __align__(256) uint8_t scratch[ENGRAM_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of `scratch` (looked up on the first call on
+// that device); ENGRAM_EHIP if the runtime cannot give its address.
+static int scratch_of_current_device(uint8_t** p) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return ENGRAM_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return ENGRAM_EUNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return ENGRAM_EHIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *p = (uint8_t*)g_scratch_ptr[dev];
+  return ENGRAM_OK;
+}
+
+int engram_forward_noalloc(const engram_forward_args* a, void* stream) {
+  int32_t K = 0, N = 0;
+  int st = check_forward_args(a, &K, &N);
+  if (st != ENGRAM_OK || a->T == 0) return st;
+  // the workspace engram_forward would need, without its flag area (which
+  // only engram_forward_single_launch uses)
+  const size_t need = engram_forward_workspace_size(a) - kSyncBytes;
+  if (need > (size_t)ENGRAM_NOALLOC_SCRATCH_BYTES) return ENGRAM_ENOSPACE;
+  uint8_t* p = nullptr;
+  st = scratch_of_current_device(&p);
+  if (st != ENGRAM_OK) return st;
+  return run_forward(a, K, N, p, (hipStream_t)stream);
 }
 
 int engram_forward_single_launch(const engram_forward_args* a, void* workspace,

@@ -16,7 +16,8 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libengram.so")
 
-ENGRAM_OK, ENGRAM_EINVAL, ENGRAM_EUNSUPPORTED, ENGRAM_EHIP = 0, 1, 2, 3
+ENGRAM_OK, ENGRAM_EINVAL, ENGRAM_EUNSUPPORTED, ENGRAM_EHIP, ENGRAM_ENOSPACE = 0, 1, 2, 3, 4
+NOALLOC_SCRATCH_BYTES = 32 << 20
 W_BF16, W_MXFP8 = 0, 1
 FORWARD_STORE_KV = 1
 
@@ -56,6 +57,7 @@ EXPORTS = {
     "engram_forward_workspace_size": (_sz, [ctypes.POINTER(ForwardArgs)]),
     "engram_forward": (_i32, [ctypes.POINTER(ForwardArgs), _vp, _sz, _vp]),
     "engram_forward_single_launch": (_i32, [ctypes.POINTER(ForwardArgs), _vp, _sz, _vp]),
+    "engram_forward_noalloc": (_i32, [ctypes.POINTER(ForwardArgs), _vp]),
     "engram_probe_out_bytes": (_sz, []),
     "engram_probe_mfma": (_i32, [_i32, _i32, _vp, ctypes.POINTER(ctypes.c_double), _vp]),
     "engram_probe_read": (_i32, [_vp, _sz, _vp, _vp]),
@@ -89,7 +91,7 @@ class EngramError(RuntimeError):
 def _check(status: int) -> None:
     if status != ENGRAM_OK:
         msg = load_library().engram_status_string(status).decode()
-        cls = ValueError if status in (ENGRAM_EINVAL, ENGRAM_EUNSUPPORTED) else EngramError
+        cls = ValueError if status in (ENGRAM_EINVAL, ENGRAM_EUNSUPPORTED, ENGRAM_ENOSPACE) else EngramError
         raise cls(f"libengram: {msg} (status {status})")
 
 
@@ -299,6 +301,24 @@ def forward(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask
     ws_bytes = 0 if workspace is None else workspace.numel()
     fn = L.engram_forward_single_launch if single_launch else L.engram_forward
     _check(fn(ctypes.byref(args), _ptr(workspace), ws_bytes, _stream()))
+    return out
+
+
+def forward_noalloc(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask=None,
+                    eps=1e-6, clamp=1e-6, out=None, gate_out=None, err_flag=None, table_scales=None,
+                    store_kv=False):
+    """engram_forward_noalloc: the forward on the library's fixed device
+    scratch (no workspace argument; ValueError when the input needs more than
+    NOALLOC_SCRATCH_BYTES). ``out`` is allocated here when not given."""
+    L = load_library()
+    for t, n in ((table, "table"), (w, "w"), (hidden, "hidden"),
+                 (q_weight, "q_weight"), (k_weight, "k_weight")):
+        _dense(t, n)
+    if out is None:
+        out = torch.empty_like(hidden)
+    args = forward_args(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask,
+                        eps, clamp, out, gate_out, err_flag, table_scales, store_kv)
+    _check(L.engram_forward_noalloc(ctypes.byref(args), _stream()))
     return out
 
 

@@ -34,14 +34,16 @@
 extern "C" {
 #endif
 
-#define ENGRAM_ABI_VERSION 4
+#define ENGRAM_ABI_VERSION 5
 
 /* Status codes. */
 enum {
   ENGRAM_OK = 0,
   ENGRAM_EINVAL = 1,       /* NULL required pointer, bad size, misalignment */
   ENGRAM_EUNSUPPORTED = 2, /* a valid shape the library has no kernel for */
-  ENGRAM_EHIP = 3          /* a HIP runtime error at launch */
+  ENGRAM_EHIP = 3,         /* a HIP runtime error at launch */
+  ENGRAM_ENOSPACE = 4      /* engram_forward_noalloc: the call needs more than
+                              ENGRAM_NOALLOC_SCRATCH_BYTES of scratch */
 };
 
 /* wkv weight formats. */
@@ -294,6 +296,27 @@ int engram_forward(const engram_forward_args* a, void* workspace,
  */
 int engram_forward_single_launch(const engram_forward_args* a, void* workspace,
                                  size_t workspace_bytes, void* stream);
+
+/*
+ * engram_forward_noalloc -- engram_forward for callers that cannot allocate
+ *   device memory (code under HIP graph capture, tight serving loops,
+ *   harnesses that forbid hipMalloc): the same launches and results, bit for
+ *   bit, as engram_forward with a caller workspace, but the scratch (staged
+ *   rows, kv or value + gate partials, MXFP8 staging) lives in a fixed
+ *   buffer of ENGRAM_NOALLOC_SCRATCH_BYTES inside the library, one per GPU,
+ *   held until the process ends. The call allocates and frees nothing.
+ *
+ *   Arguments, checks and errors as engram_forward, plus ENGRAM_ENOSPACE
+ *   (nothing launched) when engram_forward_workspace_size(a) - 64 KiB
+ *   exceeds ENGRAM_NOALLOC_SCRATCH_BYTES: at dim 4096 and K 2048 that is
+ *   about 740 tokens; every decode batch (T <= 64) fits.
+ *   Every call on one GPU uses that GPU's one buffer and leaves its last
+ *   contents there (nothing in it has to start at zero). Calls that overlap
+ *   on one GPU (different streams or threads without ordering between them)
+ *   race on the buffer and give undefined results: order them on one stream.
+ */
+#define ENGRAM_NOALLOC_SCRATCH_BYTES (32u << 20)
+int engram_forward_noalloc(const engram_forward_args* a, void* stream);
 
 /*
  * Measurement probes. Not steps of the layer: they measure the rates this

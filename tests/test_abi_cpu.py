@@ -77,11 +77,12 @@ def test_forward_args_layout_matches_c():
 
 
 def test_status_strings_and_version(lib):
-    assert lib.engram_abi_version() == 4
+    assert lib.engram_abi_version() == 5
     assert lib.engram_status_string(0) == b"ok"
     assert lib.engram_status_string(1) == b"invalid argument"
     assert lib.engram_status_string(2) == b"unsupported shape"
     assert lib.engram_status_string(3) == b"HIP runtime error"
+    assert lib.engram_status_string(4) == b"input larger than the fixed scratch buffer"
     assert lib.engram_status_string(99) == b"unknown status"
 
 
