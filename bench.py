@@ -6,17 +6,24 @@ head_dim 128 (K = 2048, N = 20480), bf16 tables (33.6 M rows, 8.6 GB,
 HBM-resident) and bf16 wkv, Zipf(1.1) ids, no mask. Inputs are seeded and
 synthetic and already resident in HBM when the timed region starts.
 
-Prints one JSON line. ``value`` is prefill tokens/s; ``decode_t16`` carries
-the decode workload (T = 16, MXFP8 wkv) measured cold: 16 copies of the
-weight are rotated so no step finds it in the 256 MB Infinity Cache.
-``roofline`` is the dominant kernel (the wkv GEMM with the gate epilogue that
-the default forward launches, MFMA-bound) with its duration taken from HIP
-events on the launch stream, around calls of engram_wkv_gate_partials in the
-same launch configuration, made just before the timed steps.
-``cpu_baseline`` is the CPU oracle on a bounded sample of the same workload.
-``measured_peaks`` are ceilings measured on the same GPU with the library's
-probes (register-only MFMA loops, a streaming read and copy of 4 GiB); each
-fraction of a datasheet peak has a ``frac_of_measured`` beside it.
+The timed region comes right after the W warm-up steps, with nothing else
+run in between: K forwards between two synchronizations. Everything else is
+measured afterwards.
+
+Prints one JSON line. ``value`` is prefill tokens/s. ``roofline`` is the
+dominant kernel (the wkv GEMM with the gate epilogue that the default
+forward launches, MFMA-bound), its duration taken from HIP events on the
+launch stream around calls of engram_wkv_gate_partials in the same launch
+configuration. ``configs`` has one row per workload the layer is specified
+on (tiny, mid, prefill, decode at T = 1, 4, 16, 64, long): forward time,
+tokens/s, the bound and the fraction of that bound's peak. The decode rows
+are measured cold: 16 copies of the 40 MiB weight are rotated so no step
+finds its weight in the 256 MB Infinity Cache. ``kernels`` breaks the
+prefill step down (gather, GEMM, gate), each with its fraction of peak.
+``cpu_baseline`` is the CPU oracle on a bounded sample of the prefill
+workload. ``measured_peaks`` are ceilings measured on the same GPU with the
+library's probes; each fraction of a datasheet peak that has a measured
+counterpart is also given against it.
 """
 
 from __future__ import annotations
@@ -37,6 +44,7 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 FP8_PEAK_TFLOPS = 5000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+DECODE_COPIES = 16
 
 
 def _source_sha(rel: str) -> str:
@@ -58,8 +66,8 @@ def _traffic(kernel: str, src: str):
 
 
 def _events_time(fn, iters, stream):
-    """Average duration (ms) of fn() over iters launches, from HIP events on
-    the stream the work is enqueued on."""
+    """Per-call durations (ms) of fn(i), i < iters, from HIP events recorded
+    on the stream the work is enqueued on."""
     import torch
 
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(iters)]
@@ -78,7 +86,34 @@ def _pct(v, q):
     return v[min(len(v) - 1, max(0, int(round(q / 100.0 * (len(v) - 1)))))]
 
 
+def _us(v):
+    """median, p10, p90 of a list of ms, in us."""
+    return [round(statistics.median(v) * 1e3, 2), round(_pct(v, 10) * 1e3, 2), round(_pct(v, 90) * 1e3, 2)]
+
+
+def alg_bytes(wl) -> int:
+    """Algorithmic HBM bytes of one forward: the weight (+ E8M0 scales), the
+    ids, the gathered table rows, hidden in and out, q and k, the mask. kv
+    and the staged rows are the implementation's own traffic, not counted."""
+    w = wl.N * wl.K * (2 if wl.w_format == "bf16" else 1)
+    if wl.w_format != "bf16":
+        w += (wl.N // 32) * (wl.K // 32)
+    rows = wl.T * wl.C * wl.head_dim * 2
+    ids = wl.T * wl.C * 4
+    hid = 2 * wl.T * wl.hc * wl.dim * 2
+    qk = 2 * wl.hc * wl.dim * 2
+    mask = wl.T if wl.mask_frac is not None else 0
+    return w + rows + ids + hid + qk + mask
+
+
+def _plan(E, inp, wl, out, **kw):
+    return E.ForwardPlan(inp["table"], inp["ids"], inp["w"], inp["w_scales"], inp["hidden"], inp["q"],
+                         inp["k"], inp["mask"], wl.eps, wl.clamp, out=out, **kw)
+
+
 def bench_prefill(steps, warmup):
+    """The headline: W warm-up forwards, then K timed forwards; afterwards
+    the per-kernel durations of the same step."""
     import torch
 
     from gram_memory_layer_engram_amd import engram as E
@@ -88,25 +123,22 @@ def bench_prefill(steps, warmup):
     inp = W.make_inputs(wl, "cuda")
     stream = torch.cuda.current_stream()
     out = torch.empty_like(inp["hidden"])
-    args = E.forward_args(inp["table"], inp["ids"], inp["w"], None, inp["hidden"], inp["q"],
-                          inp["k"], None, wl.eps, wl.clamp, out)
-    ws = torch.empty(E.forward_workspace_size(args), dtype=torch.uint8, device="cuda")
-
-    def fwd(_=0, store_kv=False):
-        E.forward(inp["table"], inp["ids"], inp["w"], None, inp["hidden"], inp["q"], inp["k"],
-                  None, wl.eps, wl.clamp, out=out, workspace=ws, store_kv=store_kv)
-
+    plan = _plan(E, inp, wl, out)
     for _ in range(warmup):
-        fwd()
+        plan.run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        plan.run()
+    torch.cuda.synchronize()
+    dt = (time.perf_counter() - t0) / steps
 
-    # Per-kernel durations, before the timed steps so that those start from
-    # the clocks and caches of a running loop: the default forward (the
-    # GEMM's gate epilogue, keys never stored) and the store-kv forward
-    # (kv stored, plain gate), alternated call by call so both see the same
-    # clocks; then the steps of each route called one by one through
-    # pre-marshalled C calls. All event-timed on the launch stream.
-    t_both = _events_time(lambda i: fwd(i, i % 2 == 1), 2 * steps, stream)
-    t_fwd, t_fwd_kv = t_both[0::2], t_both[1::2]
+    # per-kernel durations of the same step, each event-timed on the launch
+    # stream through pre-marshalled C calls
+    n = max(steps, 20)
+    t_fwd = _events_time(lambda i: plan.run(), n, stream)
+    plan_kv = _plan(E, inp, wl, out, store_kv=True, workspace=plan.workspace)
+    t_fwd_kv = _events_time(lambda i: plan_kv.run(), n, stream)
     rows = torch.empty((wl.T, wl.C, wl.head_dim), dtype=torch.bfloat16, device="cuda")
     kv = torch.empty((wl.T, wl.N), dtype=torch.bfloat16, device="cuda")
     x = rows.view(wl.T, wl.K)
@@ -115,7 +147,7 @@ def bench_prefill(steps, warmup):
     ids = inp["ids"]
     look = (inp["table"].data_ptr(), inp["table"].shape[0], wl.head_dim, ids.data_ptr(), ids.stride(0),
             ids.stride(1), wl.T, wl.C, rows.data_ptr(), None, sp)
-    t_lookup = _events_time(lambda i: L.engram_lookup(*look), steps, stream)
+    t_lookup = _events_time(lambda i: L.engram_lookup(*look), n, stream)
     value = torch.empty((wl.T, wl.dim), dtype=torch.bfloat16, device="cuda")
     parts = torch.empty((wl.hc, wl.T, wl.dim // 256, 2), dtype=torch.float32, device="cuda")
     fused = (x.data_ptr(), wl.T, wl.K, inp["w"].data_ptr(), None, E.W_BF16, wl.hc, wl.dim,
@@ -123,100 +155,133 @@ def bench_prefill(steps, warmup):
              parts.data_ptr(), None, 0, sp)
     if L.engram_wkv_gate_partials(*fused) != 0:
         raise RuntimeError("engram_wkv_gate_partials refused the prefill shapes")
-    t_fused = _events_time(lambda i: L.engram_wkv_gate_partials(*fused), steps, stream)
-    t_wkv = _events_time(lambda i: E.wkv(x, inp["w"], kv=kv), steps, stream)
-    t_gate = _events_time(lambda i: E.gate(inp["hidden"], kv, inp["q"], inp["k"], None, wl.eps,
-                                           wl.clamp, out=out), steps, stream)
-
-    # the timed region: K forward steps between two synchronizations
-    fwd()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        fwd()
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / steps
+    t_fused = _events_time(lambda i: L.engram_wkv_gate_partials(*fused), n, stream)
+    wkv = (x.data_ptr(), wl.T, wl.K, inp["w"].data_ptr(), None, E.W_BF16, wl.N, kv.data_ptr(), None, 0, sp)
+    t_wkv = _events_time(lambda i: L.engram_wkv(*wkv), n, stream)
+    gate = (inp["hidden"].data_ptr(), kv.data_ptr(), inp["q"].data_ptr(), inp["k"].data_ptr(), None, wl.T,
+            wl.hc, wl.dim, wl.eps, wl.clamp, out.data_ptr(), None, sp)
+    t_gate = _events_time(lambda i: L.engram_gate(*gate), n, stream)
 
     # the same gather from the table stored as fp8 (e4m3 + ue8m0 per 32), dequantized on lookup
-    del inp["table"]
+    del plan, plan_kv, inp["table"]
     torch.cuda.empty_cache()
     codes, scales = W.make_table_fp8(wl, "cuda")
     look8 = (codes.data_ptr(), scales.data_ptr(), codes.shape[0], wl.head_dim, ids.data_ptr(), ids.stride(0),
              ids.stride(1), wl.T, wl.C, rows.data_ptr(), None, sp)
     for _ in range(warmup):
         L.engram_lookup_fp8(*look8)
-    t_lookup8 = _events_time(lambda i: L.engram_lookup_fp8(*look8), steps, stream)
+    t_lookup8 = _events_time(lambda i: L.engram_lookup_fp8(*look8), n, stream)
+    del codes, scales, inp
+    torch.cuda.empty_cache()
     return wl, dt, {"lookup": t_lookup, "wkv_gate_partials": t_fused, "wkv": t_wkv, "gate": t_gate,
                     "lookup_fp8": t_lookup8, "forward": t_fwd, "forward_store_kv": t_fwd_kv}
 
 
-def bench_decode(steps, warmup, copies=16):
+def bench_small(name, iters=200, warmup=20):
+    """tiny and mid: event-timed forwards (warm: these inputs fit the
+    Infinity Cache, as they would in a running model), and for mid the
+    default forward's projection GEMM on its own."""
     import torch
 
     from gram_memory_layer_engram_amd import engram as E
     from gram_memory_layer_engram_amd import workloads as W
 
-    wl = W.WORKLOADS["decode_t16"]
-    base = W.make_inputs(wl, "cuda")
-    # cold cache: distinct weight copies (16 x 40 MiB) and per-copy activations
-    sets = []
-    for v in range(copies):
-        sets.append({
-            "w": base["w"].clone(), "w_scales": base["w_scales"].clone(),
-            "ids": torch.from_numpy(W.make_ids(wl, variant=v)).cuda(),
-            "hidden": W.make_hidden(wl, device="cuda", variant=v),
-            "mask": torch.from_numpy(W.make_mask(wl, variant=v)).cuda(),
-        })
-    out = torch.empty_like(base["hidden"])
+    wl = W.WORKLOADS[name]
+    inp = W.make_inputs(wl, "cuda")
     stream = torch.cuda.current_stream()
-    # one prepared forward per rotated set: a step is a single C call
-    plans = [E.ForwardPlan(base["table"], s["ids"], s["w"], s["w_scales"], s["hidden"], base["q"],
-                           base["k"], s["mask"], wl.eps, wl.clamp, out=out) for s in sets]
+    out = torch.empty_like(inp["hidden"])
+    plan = _plan(E, inp, wl, out)
+    for _ in range(warmup):
+        plan.run()
+    t_fwd = _events_time(lambda i: plan.run(), iters, stream)
+    res = {"forward": t_fwd}
+    if name == "mid":
+        L = E.load_library()
+        sp = stream.cuda_stream
+        x = E.lookup(inp["table"], inp["ids"]).view(wl.T, wl.K)
+        value = torch.empty((wl.T, wl.dim), dtype=torch.bfloat16, device="cuda")
+        parts = torch.empty((wl.hc, wl.T, wl.dim // 256, 2), dtype=torch.float32, device="cuda")
+        fused = (x.data_ptr(), wl.T, wl.K, inp["w"].data_ptr(), None, E.W_BF16, wl.hc, wl.dim,
+                 inp["hidden"].data_ptr(), inp["q"].data_ptr(), inp["k"].data_ptr(), value.data_ptr(),
+                 parts.data_ptr(), None, 0, sp)
+        if L.engram_wkv_gate_partials(*fused) != 0:
+            raise RuntimeError("engram_wkv_gate_partials refused the mid shapes")
+        res["wkv_gate_partials"] = _events_time(lambda i: L.engram_wkv_gate_partials(*fused), iters, stream)
+    del inp, plan
+    torch.cuda.empty_cache()
+    return wl, res
 
-    def fwd(i):
-        plans[i % copies].run()
 
-    for i in range(warmup):
-        fwd(i)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(steps):
-        fwd(i)
-    torch.cuda.synchronize()
-    dt = (time.perf_counter() - t0) / steps
+def bench_decode(steps, warmup, copies=DECODE_COPIES):
+    """Decode at T = 1, 4, 16, 64 (MXFP8 wkv [20480, 2048]), cold: `copies`
+    weight copies (40 MiB each, together well past the 256 MB Infinity
+    Cache) and per-copy ids / hidden / mask rotated call by call."""
+    import torch
 
-    # the GEMV alone (quantize included: that is engram_wkv), cold
-    x = torch.empty((wl.T, wl.K), dtype=torch.bfloat16, device="cuda")
-    E.lookup(base["table"], base["ids"], rows_out=x.view(wl.T, wl.C, wl.head_dim))
-    kv = torch.empty((wl.T, wl.N), dtype=torch.bfloat16, device="cuda")
-    wws = torch.empty(max(1, E.load_library().engram_wkv_workspace_size(wl.T, wl.K, wl.N, E.W_MXFP8)),
-                      dtype=torch.uint8, device="cuda")
-    # engram_wkv through a pre-marshalled C call (the Python wrapper's own
-    # checks would otherwise leave the GPU idle between launches)
+    from gram_memory_layer_engram_amd import engram as E
+    from gram_memory_layer_engram_amd import workloads as W
+
+    base_wl = W.WORKLOADS["decode_t16"]
+    table = W.make_table(base_wl, "cuda")
+    w0, ws0 = W.make_weight(base_wl, "cuda")
+    q, k = W.make_qk(base_wl, "cuda")
+    weights = [(w0.clone(), ws0.clone()) for _ in range(copies)]
+    del w0, ws0
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
     L = E.load_library()
-    sptr = stream.cuda_stream
-    wkv_args = [(x.data_ptr(), wl.T, wl.K, st["w"].data_ptr(), st["w_scales"].data_ptr(), E.W_MXFP8, wl.N,
-                 kv.data_ptr(), wws.data_ptr(), wws.numel(), sptr) for st in sets]
-    t_wkv = _events_time(lambda i: L.engram_wkv(*wkv_args[i % copies]), steps, stream)
-    # the measured ceiling for that weight stream: one streaming-read launch
-    # over the same rotated copies
     probe = E.probe_out()
-    read_args = [(st["w"].data_ptr(), st["w"].numel(), probe.data_ptr(), sptr) for st in sets]
-    t_read = _events_time(lambda i: L.engram_probe_read(*read_args[i % copies]), steps, stream)
-    t_fwd = _events_time(fwd, steps, stream)
-    # the single-launch variant of the same forward, same rotation
-    plans_1 = [E.ForwardPlan(base["table"], s["ids"], s["w"], s["w_scales"], s["hidden"], base["q"],
-                             base["k"], s["mask"], wl.eps, wl.clamp, out=out, single_launch=True) for s in sets]
-    for i in range(warmup):
-        plans_1[i % copies].run()
-    t_one = _events_time(lambda i: plans_1[i % copies].run(), steps, stream)
-    return wl, dt, {"wkv": t_wkv, "forward": t_fwd, "single_launch": t_one, "read_w": t_read}
+    res = {}
+    for T in (1, 4, 16, 64):
+        wl = W.WORKLOADS[f"decode_t{T}"]
+        sets = []
+        for v in range(copies):
+            m = W.make_mask(wl, variant=v)
+            sets.append({"ids": torch.from_numpy(W.make_ids(wl, variant=v)).cuda(),
+                         "hidden": W.make_hidden(wl, device="cuda", variant=v),
+                         "mask": torch.from_numpy(m).cuda()})
+        out = torch.empty_like(sets[0]["hidden"])
+        plans = [E.ForwardPlan(table, s["ids"], weights[i][0], weights[i][1], s["hidden"], q, k, s["mask"],
+                               wl.eps, wl.clamp, out=out) for i, s in enumerate(sets)]
+        for i in range(warmup):
+            plans[i % copies].run()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            plans[i % copies].run()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) / steps
+        t_fwd = _events_time(lambda i: plans[i % copies].run(), steps, stream)
+        # the projection alone (engram_wkv: MX quantize + decode GEMV), same rotation
+        x = E.lookup(table, sets[0]["ids"]).view(T, wl.K)
+        kv = torch.empty((T, wl.N), dtype=torch.bfloat16, device="cuda")
+        wws = torch.empty(max(1, L.engram_wkv_workspace_size(T, wl.K, wl.N, E.W_MXFP8)), dtype=torch.uint8,
+                          device="cuda")
+        wkv_args = [(x.data_ptr(), T, wl.K, wc.data_ptr(), wsc.data_ptr(), E.W_MXFP8, wl.N, kv.data_ptr(),
+                     wws.data_ptr(), wws.numel(), sp) for wc, wsc in weights]
+        t_wkv = _events_time(lambda i: L.engram_wkv(*wkv_args[i % copies]), steps, stream)
+        r = {"forward": t_fwd, "wall_s": wall, "wkv": t_wkv}
+        if T == 16:
+            # the measured ceiling for the weight stream: one streaming-read
+            # launch over the same rotated copies; and the single-launch forward
+            read_args = [(wc.data_ptr(), wc.numel(), probe.data_ptr(), sp) for wc, _ in weights]
+            r["read_w"] = _events_time(lambda i: L.engram_probe_read(*read_args[i % copies]), steps, stream)
+            plans1 = [E.ForwardPlan(table, s["ids"], weights[i][0], weights[i][1], s["hidden"], q, k, s["mask"],
+                                    wl.eps, wl.clamp, out=out, single_launch=True) for i, s in enumerate(sets)]
+            for i in range(warmup):
+                plans1[i % copies].run()
+            r["single_launch"] = _events_time(lambda i: plans1[i % copies].run(), steps, stream)
+        res[T] = (wl, r)
+        del sets, plans, x, kv
+    del table, weights
+    torch.cuda.empty_cache()
+    return res
 
 
 def bench_long(steps=5, warmup=2):
     """The long-prefill workload (T 32768, dim 7168, K 3072, MXFP8 wkv, Zipf
     ids, 10% masked): event-timed forward and projection (quantize + GEMM),
-    reported beside the headline."""
+    and the MXFP8 activation quantize on its own."""
     import torch
 
     from gram_memory_layer_engram_amd import engram as E
@@ -226,8 +291,7 @@ def bench_long(steps=5, warmup=2):
     inp = W.make_inputs(wl, "cuda")
     stream = torch.cuda.current_stream()
     out = torch.empty_like(inp["hidden"])
-    plan = E.ForwardPlan(inp["table"], inp["ids"], inp["w"], inp["w_scales"], inp["hidden"], inp["q"],
-                         inp["k"], inp["mask"], wl.eps, wl.clamp, out=out)
+    plan = _plan(E, inp, wl, out)
     for _ in range(warmup):
         plan.run()
     t_fwd = _events_time(lambda i: plan.run(), steps, stream)
@@ -237,7 +301,6 @@ def bench_long(steps=5, warmup=2):
     for _ in range(warmup):
         E.wkv(x, inp["w"], inp["w_scales"], kv=kv)
     t_wkv = _events_time(lambda i: E.wkv(x, inp["w"], inp["w_scales"], kv=kv), steps, stream)
-    # the MXFP8 activation quantize alone (engram_mx_quantize) on the same rows
     xq = torch.empty((wl.T, wl.K), dtype=torch.uint8, device="cuda")
     xs = torch.empty((wl.T, wl.K // 32), dtype=torch.uint8, device="cuda")
     L = E.load_library()
@@ -245,6 +308,8 @@ def bench_long(steps=5, warmup=2):
     if L.engram_mx_quantize(*qargs) != 0:
         raise RuntimeError("engram_mx_quantize refused the long-prefill rows")
     t_q = _events_time(lambda i: L.engram_mx_quantize(*qargs), max(steps, 20), stream)
+    del inp, plan, x, kv, xq, xs
+    torch.cuda.empty_cache()
     return wl, {"forward": t_fwd, "wkv": t_wkv, "mx_quantize": t_q}
 
 
@@ -334,6 +399,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="only the prefill forward and its kernels (for profiler runs)")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 512 MiB device copy (reference for the HBM byte counters)")
     a = ap.parse_args()
@@ -362,7 +429,6 @@ def main():
     E.load_library()
 
     wl, dt, kt = bench_prefill(a.steps, a.warmup)
-    med = {k: statistics.median(v) for k, v in kt.items()}
     avg = {k: statistics.fmean(v) for k, v in kt.items()}
     flops = 2.0 * wl.T * wl.K * wl.N
     fused_s = avg["wkv_gate_partials"] * 1e-3
@@ -379,72 +445,102 @@ def main():
     lookup_bytes = wl.T * wl.C * (4 + 2 * 2 * wl.head_dim)
     lookup8_bytes = wl.T * wl.C * (4 + wl.head_dim + wl.head_dim // 32 + 2 * wl.head_dim)
     gate_bytes = wl.T * (2 * wl.hc * wl.dim + (wl.hc + 1) * wl.dim) * 2
+    gbs = lambda b, key: b / (avg[key] * 1e-3) / 1e9  # noqa: E731
     kernels = {
         "lookup_us": round(avg["lookup"] * 1e3, 2),
-        "lookup_GBs": round(lookup_bytes / (avg["lookup"] * 1e-3) / 1e9, 1),
+        "lookup_GBs": round(gbs(lookup_bytes, "lookup"), 1),
+        "lookup_hbm_frac": round(gbs(lookup_bytes, "lookup") / HBM_PEAK_GBS, 4),
         "lookup_fp8_table_us": round(avg["lookup_fp8"] * 1e3, 2),
-        "lookup_fp8_table_GBs": round(lookup8_bytes / (avg["lookup_fp8"] * 1e-3) / 1e9, 1),
+        "lookup_fp8_table_GBs": round(gbs(lookup8_bytes, "lookup_fp8"), 1),
+        "lookup_fp8_table_hbm_frac": round(gbs(lookup8_bytes, "lookup_fp8") / HBM_PEAK_GBS, 4),
         "wkv_gate_partials_us": round(avg["wkv_gate_partials"] * 1e3, 2),
-        "wkv_gate_partials_us_p10_p90": [round(_pct(kt["wkv_gate_partials"], 10) * 1e3, 2),
-                                         round(_pct(kt["wkv_gate_partials"], 90) * 1e3, 2)],
-        "wkv_us": round(avg["wkv"] * 1e3, 2), "wkv_us_median": round(med["wkv"] * 1e3, 2),
-        "wkv_us_p10_p90": [round(_pct(kt["wkv"], 10) * 1e3, 2), round(_pct(kt["wkv"], 90) * 1e3, 2)],
+        "wkv_gate_partials_us_med_p10_p90": _us(kt["wkv_gate_partials"]),
+        "wkv_gate_partials_mfma_frac": roofline["frac"],
+        "wkv_us": round(avg["wkv"] * 1e3, 2),
+        "wkv_us_med_p10_p90": _us(kt["wkv"]),
         "wkv_mfma_frac": round(flops / (avg["wkv"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
         "gate_us": round(avg["gate"] * 1e3, 2),
-        "gate_us_p10_p90": [round(_pct(kt["gate"], 10) * 1e3, 2), round(_pct(kt["gate"], 90) * 1e3, 2)],
-        "gate_GBs": round(gate_bytes / (avg["gate"] * 1e-3) / 1e9, 1),
+        "gate_us_med_p10_p90": _us(kt["gate"]),
+        "gate_GBs": round(gbs(gate_bytes, "gate"), 1),
+        "gate_hbm_frac": round(gbs(gate_bytes, "gate") / HBM_PEAK_GBS, 4),
         "forward_us_events": round(avg["forward"] * 1e3, 2),
+        "forward_us_med_p10_p90": _us(kt["forward"]),
         "forward_store_kv_us_events": round(avg["forward_store_kv"] * 1e3, 2),
     }
+    if a.headline_only:
+        print(json.dumps({"metric": METRIC, "value": round(wl.T / dt, 1), "ms_per_step": round(dt * 1e3, 4),
+                          "roofline": roofline, "kernels": kernels}), flush=True)
+        return
 
-    dwl, ddt, dkt = bench_decode(max(a.steps, 100), a.warmup)
-    d_wkv = statistics.fmean(dkt["wkv"]) * 1e-3
-    d_fwd = statistics.fmean(dkt["forward"]) * 1e-3
-    w_bytes = dwl.N * dwl.K + dwl.N * dwl.K // 1024
-    d_alg = w_bytes + dwl.T * dwl.C * (4 + 2 * 2 * dwl.head_dim) + dwl.T * 2 * dwl.hc * dwl.dim * 2 \
-        + 2 * dwl.hc * dwl.dim * 2 + dwl.T
-    decode = {
-        "workload": "decode T=16, dim 4096, MXFP8 wkv [20480, 2048] (40 MiB), 16 weight copies rotated",
-        "value": round(dwl.T / ddt, 1), "unit": "tokens/s", "ms_per_step": round(ddt * 1e3, 4),
-        "forward_us_events": round(d_fwd * 1e6, 2),
-        "forward_us_median_p10_p90": [round(statistics.median(dkt["forward"]) * 1e3, 2),
-                                      round(_pct(dkt["forward"], 10) * 1e3, 2),
-                                      round(_pct(dkt["forward"], 90) * 1e3, 2)],
-        "forward_hbm_frac": round(d_alg / d_fwd / 1e9 / HBM_PEAK_GBS, 4),
-        "single_launch_us_events": round(statistics.fmean(dkt["single_launch"]) * 1e3, 2),
-        "wkv_us": round(d_wkv * 1e6, 2),
-        "wkv_GBs": round((w_bytes + dwl.T * dwl.N * 2) / d_wkv / 1e9, 1),
-        "wkv_hbm_frac": round((w_bytes + dwl.T * dwl.N * 2) / d_wkv / 1e9 / HBM_PEAK_GBS, 4),
+    configs = {}
+    pf_alg = alg_bytes(wl)
+    configs["prefill"] = {
+        "T": wl.T, "forward_us": round(dt * 1e6, 2), "tokens_per_s": round(wl.T / dt, 1),
+        "bound": "mfma", "frac": roofline["frac"],
+        "frac_kernel": "projection GEMM with the gate epilogue, of 2.5 PFLOP/s bf16",
+        "alg_bytes": pf_alg, "alg_GBs": round(pf_alg / dt / 1e9, 1),
     }
+    for name in ("tiny", "mid"):
+        swl, sr = bench_small(name)
+        f = statistics.median(sr["forward"]) * 1e-3
+        ab = alg_bytes(swl)
+        row = {"T": swl.T, "forward_us": round(f * 1e6, 2), "forward_us_med_p10_p90": _us(sr["forward"]),
+               "tokens_per_s": round(swl.T / f, 1), "alg_bytes": ab, "alg_GBs": round(ab / f / 1e9, 1)}
+        if name == "tiny":
+            # 0.56 MB and 25 MFLOP: three launches' fixed cost, not bandwidth or MFMA, bound it
+            row.update({"bound": "launch", "hbm_frac": round(ab / f / 1e9 / HBM_PEAK_GBS, 5)})
+        else:
+            g = statistics.median(sr["wkv_gate_partials"]) * 1e-3
+            gfl = 2.0 * swl.T * swl.K * swl.N
+            row.update({"bound": "mfma", "wkv_gate_partials_us": round(g * 1e6, 2),
+                        "frac": round(gfl / g / 1e12 / BF16_PEAK_TFLOPS, 4),
+                        "frac_kernel": "projection GEMM with the gate epilogue, of 2.5 PFLOP/s bf16"})
+        configs[name] = row
+
+    dec = bench_decode(max(a.steps, 100), a.warmup)
+    for T, (dwl, r) in dec.items():
+        f = statistics.median(r["forward"]) * 1e-3
+        wk = statistics.median(r["wkv"]) * 1e-3
+        ab = alg_bytes(dwl)
+        w_bytes = dwl.N * dwl.K + (dwl.N // 32) * (dwl.K // 32)
+        row = {"T": T, "forward_us": round(f * 1e6, 2), "forward_us_med_p10_p90": _us(r["forward"]),
+               "forward_us_wall": round(r["wall_s"] * 1e6, 2),
+               "tokens_per_s": round(T / f, 1), "bound": "hbm", "alg_bytes": ab,
+               "frac": round(ab / f / 1e9 / HBM_PEAK_GBS, 4),
+               "frac_kernel": "whole forward, algorithmic bytes of 8 TB/s (cold weights)",
+               "wkv_us": round(wk * 1e6, 2),
+               "wkv_hbm_frac": round((w_bytes + T * (dwl.K + dwl.K // 32) + T * dwl.N * 2) / wk / 1e9
+                                     / HBM_PEAK_GBS, 4)}
+        if "read_w" in r:
+            rd = statistics.median(r["read_w"]) * 1e-3
+            row["read_40MiB_cold_us"] = round(rd * 1e6, 2)
+            row["wkv_us_vs_read_40MiB_cold"] = round(wk / rd, 3)
+            row["single_launch_us"] = round(statistics.median(r["single_launch"]) * 1e6 * 1e-3, 2)
+        configs[f"decode_t{T}"] = row
 
     lwl, lkt = bench_long()
+    l_fwd = statistics.median(lkt["forward"]) * 1e-3
+    l_wkv = statistics.median(lkt["wkv"]) * 1e-3
+    l_q = statistics.median(lkt["mx_quantize"]) * 1e-3
+    lflops = 2.0 * lwl.T * lwl.K * lwl.N
+    configs["long"] = {
+        "T": lwl.T, "forward_us": round(l_fwd * 1e6, 1), "tokens_per_s": round(lwl.T / l_fwd, 1),
+        "bound": "mfma", "frac": round(lflops / l_wkv / 1e12 / FP8_PEAK_TFLOPS, 4),
+        "frac_kernel": "MXFP8 projection (quantize + scaled GEMM), of 5.0 PFLOP/s",
+        "wkv_us": round(l_wkv * 1e6, 1),
+        "mx_quantize_us": round(l_q * 1e6, 2),
+        "mx_quantize_hbm_frac": round(lwl.T * (3 * lwl.K + lwl.K // 32) / l_q / 1e9 / HBM_PEAK_GBS, 4),
+    }
+
     peaks = measured_peaks()
     roofline["measured_peak"] = peaks["mfma_bf16_TFLOPs"]
     roofline["frac_of_measured"] = round(achieved / peaks["mfma_bf16_TFLOPs"], 4)
     roofline["measured_peak_source"] = "register-only bf16 MFMA loop on this GPU (engram_probe_mfma)"
     kernels["gate_frac_of_measured_2to1"] = round(kernels["gate_GBs"] / peaks["hbm_stream_2to1_GBs"], 4)
-    d_read = statistics.fmean(dkt["read_w"]) * 1e-3
-    decode["forward_frac_of_measured_read"] = round(d_alg / d_fwd / 1e9 / peaks["hbm_read_GBs"], 4)
-    decode["read_40MiB_cold_us"] = round(d_read * 1e6, 2)
-    decode["read_40MiB_cold_GBs"] = round(dwl.N * dwl.K / d_read / 1e9, 1)
-    decode["wkv_us_vs_read_40MiB_cold"] = round(d_wkv / d_read, 3)
-    l_fwd = statistics.fmean(lkt["forward"]) * 1e-3
-    l_wkv = statistics.fmean(lkt["wkv"]) * 1e-3
-    l_q = statistics.fmean(lkt["mx_quantize"]) * 1e-3
-    long = {
-        "workload": "long prefill T=32768, dim 7168, hc 4, K 3072, MXFP8 wkv [35840, 3072], Zipf ids, "
-                    "10% masked",
-        "forward_us_events": round(l_fwd * 1e6, 1),
-        "tokens_per_s": round(lwl.T / l_fwd, 1),
-        "wkv_us": round(l_wkv * 1e6, 1),
-        "wkv_mfma_frac": round(2.0 * lwl.T * lwl.K * lwl.N / l_wkv / 1e12 / FP8_PEAK_TFLOPS, 4),
-        "wkv_frac_of_measured_mfma": round(2.0 * lwl.T * lwl.K * lwl.N / l_wkv / 1e12 / peaks["mfma_mxfp8_TFLOPs"], 4),
-        # activation quantize: per token 2K bytes read, K + K/32 written
-        "mx_quantize_us": round(l_q * 1e6, 2),
-        "mx_quantize_GBs": round(lwl.T * (3 * lwl.K + lwl.K // 32) / l_q / 1e9, 1),
-        "mx_quantize_frac_of_measured_2to1": round(lwl.T * (3 * lwl.K + lwl.K // 32) / l_q / 1e9
-                                                   / peaks["hbm_stream_2to1_GBs"], 4),
-    }
+    configs["long"]["frac_of_measured"] = round(lflops / l_wkv / 1e12 / peaks["mfma_mxfp8_TFLOPs"], 4)
+    for T in (1, 4, 16, 64):
+        row = configs[f"decode_t{T}"]
+        row["frac_of_measured_read"] = round(row["frac"] * HBM_PEAK_GBS / peaks["hbm_read_GBs"], 4)
 
     cpu = None if a.no_cpu_baseline else cpu_baseline()
     line = {
@@ -455,7 +551,7 @@ def main():
         "config": {"workload": "prefill: T=8192, dim=4096, hc=4, n_hash_cols=16, head_dim=128, "
                                "bf16 tables 33556876 rows (HBM), bf16 wkv [20480, 2048], Zipf(1.1) ids, no mask",
                    "global_batch": wl.T, "parallelism": "none (1 GPU)"},
-        "roofline": roofline, "kernels": kernels, "decode_t16": decode, "long_prefill": long,
+        "roofline": roofline, "kernels": kernels, "configs": configs,
         "measured_peaks": peaks,
         "cpu_baseline": cpu,
     }
