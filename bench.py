@@ -162,6 +162,8 @@ def bench_prefill(steps, warmup):
             wl.hc, wl.dim, wl.eps, wl.clamp, out.data_ptr(), None, sp)
     t_gate = _events_time(lambda i: L.engram_gate(*gate), n, stream)
 
+    offload = bench_background_and_host_table(E, inp, wl)
+
     # the same gather from the table stored as fp8 (e4m3 + ue8m0 per 32), dequantized on lookup
     del plan, plan_kv, inp["table"]
     torch.cuda.empty_cache()
@@ -174,7 +176,98 @@ def bench_prefill(steps, warmup):
     del codes, scales, inp
     torch.cuda.empty_cache()
     return wl, dt, {"lookup": t_lookup, "wkv_gate_partials": t_fused, "wkv": t_wkv, "gate": t_gate,
-                    "lookup_fp8": t_lookup8, "forward": t_fwd, "forward_store_kv": t_fwd_kv}
+                    "lookup_fp8": t_lookup8, "forward": t_fwd, "forward_store_kv": t_fwd_kv}, offload
+
+
+def chunked_prefill(E, inp, wl, chunks, background, out, bufs, kv, main, side):
+    """One prefill forward as `chunks` token chunks in the kv-stored
+    composition (lookup -> engram_wkv -> engram_gate). background: chunk
+    c+1's lookup runs on `side` with engram_lookup_background while `main`
+    runs chunk c's projection and gate (events order each projection after
+    its gather, each gather after the projection that last read its row
+    buffer); else every step runs on `main` in order."""
+    import torch
+
+    ct = wl.T // chunks
+    gathered = [torch.cuda.Event() for _ in range(chunks)]
+    consumed = [torch.cuda.Event() for _ in range(chunks)]
+
+    def gather(c):
+        if not background:
+            E.lookup(inp["table"], inp["ids"][c * ct:(c + 1) * ct], rows_out=bufs[c % 2])
+            return
+        with torch.cuda.stream(side):
+            if c >= 2:
+                side.wait_event(consumed[c - 2])
+            E.lookup(inp["table"], inp["ids"][c * ct:(c + 1) * ct], rows_out=bufs[c % 2], background=True)
+            gathered[c].record(side)
+
+    if background:
+        side.wait_stream(main)
+        gather(0)
+    for c in range(chunks):
+        if background:
+            if c + 1 < chunks:
+                gather(c + 1)
+            main.wait_event(gathered[c])
+        else:
+            gather(c)
+        sl = slice(c * ct, (c + 1) * ct)
+        E.wkv(bufs[c % 2].view(ct, wl.K), inp["w"], kv=kv)
+        if background:
+            consumed[c].record(main)
+        E.gate(inp["hidden"][sl], kv, inp["q"], inp["k"], None if inp["mask"] is None else inp["mask"][sl],
+               wl.eps, wl.clamp, out=out[sl])
+
+
+def bench_background_and_host_table(E, inp, wl, reps=10, chunks=4):
+    """The two ways the pages move the gather off the critical path:
+    (a) the chunked prefill with background lookups on a side stream, against
+    the same chunks run in order on one stream (wall time per forward);
+    (b) the table in page-locked host memory, read over the host link by
+    the same gather: the prefill lookup (Zipf ids) and a decode-size one
+    (the first 16 tokens), with the link's achieved rate."""
+    import torch
+
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    ct = wl.T // chunks
+    bufs = [torch.empty((ct, wl.C, wl.head_dim), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    kv = torch.empty((ct, wl.N), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty_like(inp["hidden"])
+    res = {}
+    for bg in (False, True):
+        for _ in range(2):
+            chunked_prefill(E, inp, wl, chunks, bg, out, bufs, kv, main, side)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            chunked_prefill(E, inp, wl, chunks, bg, out, bufs, kv, main, side)
+        torch.cuda.synchronize()
+        res["chunked_background_us" if bg else "chunked_serial_us"] = round((time.perf_counter() - t0) / reps * 1e6, 1)
+    del bufs, kv, out
+    ht = E.HostTable(inp["table"].shape[0], wl.head_dim).copy_from(inp["table"])
+    try:
+        rows = torch.empty((wl.T, wl.C, wl.head_dim), dtype=torch.bfloat16, device="cuda")
+        E.lookup(ht, inp["ids"], rows_out=rows)
+        t = _events_time(lambda i: E.lookup(ht, inp["ids"], rows_out=rows), reps, main)
+        link = wl.T * wl.C * wl.head_dim * 2
+        res["host_table_lookup_us"] = round(statistics.median(t) * 1e3, 1)
+        res["host_table_rows_GBs"] = round(link / (statistics.median(t) * 1e-3) / 1e9, 2)
+        # decode-size gathers with the decode workload's uniform ids, 16
+        # id sets rotated so rows repeat rarely (the same table layout)
+        from gram_memory_layer_engram_amd import workloads as W
+        dwl = W.WORKLOADS["decode_t16"]
+        ids16 = [torch.from_numpy(W.make_ids(dwl, variant=v)).cuda() for v in range(16)]
+        r16 = torch.empty((16, wl.C, wl.head_dim), dtype=torch.bfloat16, device="cuda")
+        t16 = _events_time(lambda i: E.lookup(ht, ids16[i % 16], rows_out=r16), 64, main)
+        d16 = _events_time(lambda i: E.lookup(inp["table"], ids16[i % 16], rows_out=r16), 64, main)
+        res["host_table_lookup_t16_us"] = round(statistics.median(t16) * 1e3, 2)
+        res["device_table_lookup_t16_us"] = round(statistics.median(d16) * 1e3, 2)
+        res["host_table_bytes"] = inp["table"].numel() * 2
+    finally:
+        ht.close()
+    return res
 
 
 def bench_small(name, iters=200, warmup=20):
@@ -401,6 +494,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--headline-only", action="store_true",
                     help="only the prefill forward and its kernels (for profiler runs)")
+    ap.add_argument("--overlap-demo", action="store_true",
+                    help="only the chunked prefill with background lookups and the host-table gather")
     ap.add_argument("--calib-copy", action="store_true",
                     help="only run a plain 512 MiB device copy (reference for the HBM byte counters)")
     a = ap.parse_args()
@@ -428,7 +523,14 @@ def main():
 
     E.load_library()
 
-    wl, dt, kt = bench_prefill(a.steps, a.warmup)
+    if a.overlap_demo:
+        from gram_memory_layer_engram_amd import workloads as W
+        wl = W.WORKLOADS["prefill"]
+        inp = W.make_inputs(wl, "cuda")
+        print(json.dumps(bench_background_and_host_table(E, inp, wl, reps=5)), flush=True)
+        return
+
+    wl, dt, kt, offload = bench_prefill(a.steps, a.warmup)
     avg = {k: statistics.fmean(v) for k, v in kt.items()}
     flops = 2.0 * wl.T * wl.K * wl.N
     fused_s = avg["wkv_gate_partials"] * 1e-3
@@ -551,7 +653,7 @@ def main():
         "config": {"workload": "prefill: T=8192, dim=4096, hc=4, n_hash_cols=16, head_dim=128, "
                                "bf16 tables 33556876 rows (HBM), bf16 wkv [20480, 2048], Zipf(1.1) ids, no mask",
                    "global_batch": wl.T, "parallelism": "none (1 GPU)"},
-        "roofline": roofline, "kernels": kernels, "configs": configs,
+        "roofline": roofline, "kernels": kernels, "configs": configs, "gather_offload": offload,
         "measured_peaks": peaks,
         "cpu_baseline": cpu,
     }

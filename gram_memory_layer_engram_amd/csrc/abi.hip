@@ -163,6 +163,42 @@ int engram_lookup(const void* table, int64_t num_rows, int32_t head_dim,
                                   (hipStream_t)stream));
 }
 
+int engram_lookup_background(const void* table, int64_t num_rows, int32_t head_dim,
+                             const int32_t* hash_ids, int64_t ids_stride_t,
+                             int64_t ids_stride_c, int64_t T, int32_t n_cols,
+                             void* rows_out, int32_t* err_flag, void* stream) {
+  int st = check_lookup(table, num_rows, head_dim, hash_ids, ids_stride_t,
+                        ids_stride_c, T, n_cols, rows_out);
+  if (st != ENGRAM_OK || T == 0) return st;
+  // the persistent grid at half the compute units: one workgroup per two CUs
+  const int cap = std::max(1, dev_info().num_cus / 2);
+  return hip_status(launch_lookup(table, num_rows, head_dim, hash_ids, ids_stride_t,
+                                  ids_stride_c, T, n_cols, rows_out, err_flag,
+                                  (hipStream_t)stream, cap));
+}
+
+int engram_host_alloc(size_t bytes, void** host_ptr, void** device_ptr) {
+  if (!host_ptr || !device_ptr || bytes == 0) return ENGRAM_EINVAL;
+  *host_ptr = nullptr;
+  *device_ptr = nullptr;
+  void* h = nullptr;
+  if (hipHostMalloc(&h, bytes, hipHostMallocMapped | hipHostMallocPortable) != hipSuccess || !h)
+    return ENGRAM_EHIP;
+  void* d = nullptr;
+  if (hipHostGetDevicePointer(&d, h, 0) != hipSuccess || !d) {
+    (void)hipHostFree(h);
+    return ENGRAM_EHIP;
+  }
+  *host_ptr = h;
+  *device_ptr = d;
+  return ENGRAM_OK;
+}
+
+int engram_host_free(void* host_ptr) {
+  if (!host_ptr) return ENGRAM_OK;
+  return hip_status(hipHostFree(host_ptr));
+}
+
 int engram_lookup_fp8(const void* table_codes, const uint8_t* table_scales, int64_t num_rows,
                       int32_t head_dim, const int32_t* hash_ids, int64_t ids_stride_t,
                       int64_t ids_stride_c, int64_t T, int32_t n_cols, void* rows_out,

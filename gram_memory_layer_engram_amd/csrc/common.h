@@ -49,9 +49,11 @@ struct DevInfo {
 const DevInfo& dev_info();
 
 // ---- launchers (each validates nothing: the ABI layer has done that) ----
+// max_grid > 0 caps the persistent grid at that many workgroups (the
+// background lookup: half the compute units); 0 = 8 per compute unit.
 hipError_t launch_lookup(const void* table, int64_t num_rows, int head_dim,
                          const int32_t* ids, int64_t st, int64_t sc, int64_t T,
-                         int n_cols, void* out, int32_t* err, hipStream_t s);
+                         int n_cols, void* out, int32_t* err, hipStream_t s, int max_grid = 0);
 
 hipError_t launch_gate(const void* hidden, const void* kv, const void* q,
                        const void* k, const uint8_t* mask, int64_t T, int hc,

@@ -76,11 +76,11 @@ __global__ __launch_bounds__(kLookupThreads) void lookup_kernel(
 template <int CPR_T>
 hipError_t launch_cpr(const void* table, int64_t num_rows, const int32_t* ids,
                       int64_t st, int64_t sc, int64_t T, int n_cols, int cpr,
-                      void* out, int32_t* err, hipStream_t s) {
+                      void* out, int32_t* err, hipStream_t s, int max_grid) {
   const int64_t total = T * n_cols * cpr;
   const int64_t need = (total + kLookupThreads * kLookupUnroll - 1) /
                        (kLookupThreads * kLookupUnroll);
-  const int64_t cap = (int64_t)dev_info().num_cus * 8;
+  const int64_t cap = max_grid > 0 ? (int64_t)max_grid : (int64_t)dev_info().num_cus * 8;
   const int grid = (int)(need < cap ? need : cap);
   if (total <= (int64_t)UINT32_MAX)
     hipLaunchKernelGGL((lookup_kernel<CPR_T, uint32_t>), dim3(grid), dim3(kLookupThreads), 0, s,
@@ -175,18 +175,18 @@ hipError_t launch_lookup_fp8(const void* codes, const uint8_t* scales, int64_t n
 
 hipError_t launch_lookup(const void* table, int64_t num_rows, int head_dim,
                          const int32_t* ids, int64_t st, int64_t sc, int64_t T,
-                         int n_cols, void* out, int32_t* err, hipStream_t s) {
+                         int n_cols, void* out, int32_t* err, hipStream_t s, int max_grid) {
   const int cpr = head_dim / 8;
   switch (cpr) {
-    case 1: return launch_cpr<1>(table, num_rows, ids, st, sc, T, n_cols, cpr, out, err, s);
-    case 2: return launch_cpr<2>(table, num_rows, ids, st, sc, T, n_cols, cpr, out, err, s);
-    case 4: return launch_cpr<4>(table, num_rows, ids, st, sc, T, n_cols, cpr, out, err, s);
-    case 8: return launch_cpr<8>(table, num_rows, ids, st, sc, T, n_cols, cpr, out, err, s);
-    case 16: return launch_cpr<16>(table, num_rows, ids, st, sc, T, n_cols, cpr, out, err, s);
-    case 32: return launch_cpr<32>(table, num_rows, ids, st, sc, T, n_cols, cpr, out, err, s);
-    case 64: return launch_cpr<64>(table, num_rows, ids, st, sc, T, n_cols, cpr, out, err, s);
-    case 128: return launch_cpr<128>(table, num_rows, ids, st, sc, T, n_cols, cpr, out, err, s);
-    default: return launch_cpr<0>(table, num_rows, ids, st, sc, T, n_cols, cpr, out, err, s);
+    case 1: return launch_cpr<1>(table, num_rows, ids, st, sc, T, n_cols, cpr, out, err, s, max_grid);
+    case 2: return launch_cpr<2>(table, num_rows, ids, st, sc, T, n_cols, cpr, out, err, s, max_grid);
+    case 4: return launch_cpr<4>(table, num_rows, ids, st, sc, T, n_cols, cpr, out, err, s, max_grid);
+    case 8: return launch_cpr<8>(table, num_rows, ids, st, sc, T, n_cols, cpr, out, err, s, max_grid);
+    case 16: return launch_cpr<16>(table, num_rows, ids, st, sc, T, n_cols, cpr, out, err, s, max_grid);
+    case 32: return launch_cpr<32>(table, num_rows, ids, st, sc, T, n_cols, cpr, out, err, s, max_grid);
+    case 64: return launch_cpr<64>(table, num_rows, ids, st, sc, T, n_cols, cpr, out, err, s, max_grid);
+    case 128: return launch_cpr<128>(table, num_rows, ids, st, sc, T, n_cols, cpr, out, err, s, max_grid);
+    default: return launch_cpr<0>(table, num_rows, ids, st, sc, T, n_cols, cpr, out, err, s, max_grid);
   }
 }
 

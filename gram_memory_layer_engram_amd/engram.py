@@ -47,6 +47,9 @@ EXPORTS = {
     "engram_abi_version": (_i32, []),
     "engram_status_string": (ctypes.c_char_p, [_i32]),
     "engram_lookup": (_i32, [_vp, _i64, _i32, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
+    "engram_lookup_background": (_i32, [_vp, _i64, _i32, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
+    "engram_host_alloc": (_i32, [_sz, ctypes.POINTER(_vp), ctypes.POINTER(_vp)]),
+    "engram_host_free": (_i32, [_vp]),
     "engram_lookup_fp8": (_i32, [_vp, _vp, _i64, _i32, _vp, _i64, _i64, _i64, _i32, _vp, _vp, _vp]),
     "engram_mx_quantize": (_i32, [_vp, _i64, _i32, _vp, _vp, _vp]),
     "engram_wkv_workspace_size": (_sz, [_i64, _i32, _i32, _i32]),
@@ -95,12 +98,57 @@ def _check(status: int) -> None:
         raise cls(f"libengram: {msg} (status {status})")
 
 
-def _ptr(t: torch.Tensor | None) -> int | None:
+def _ptr(t) -> int | None:
     if t is None:
         return None
+    if isinstance(t, HostTable):
+        return t.device_ptr
     if not t.is_cuda:
         raise ValueError("libengram takes device tensors only")
     return t.data_ptr()
+
+
+class HostTable:
+    """A bf16 table ``[num_rows, head_dim]`` in page-locked host memory
+    mapped into the device's address space (engram_host_alloc): lookups and
+    forwards given it read the rows over the host link. ``host`` is a CPU
+    tensor on that memory for filling it (``copy_from`` copies a device
+    table in); ``device_ptr`` is what the kernels read through. Freed by
+    ``close()`` or when collected."""
+
+    def __init__(self, num_rows: int, head_dim: int, dtype=torch.bfloat16):
+        L = load_library()
+        self.shape = (int(num_rows), int(head_dim))
+        self.dtype = dtype
+        nbytes = self.shape[0] * self.shape[1] * torch.empty((), dtype=dtype).element_size()
+        h, d = _vp(), _vp()
+        _check(L.engram_host_alloc(nbytes, ctypes.byref(h), ctypes.byref(d)))
+        self._host_ptr = h.value
+        self.device_ptr = d.value
+        buf = (ctypes.c_uint8 * nbytes).from_address(self._host_ptr)
+        self.host = torch.frombuffer(buf, dtype=torch.uint8).view(dtype).view(self.shape)
+
+    def copy_from(self, table: torch.Tensor) -> "HostTable":
+        if tuple(table.shape) != self.shape or table.dtype != self.dtype:
+            raise ValueError(f"table must be {self.dtype} {self.shape}")
+        self.host.copy_(table)
+        return self
+
+    def dim(self) -> int:
+        return 2
+
+    def close(self) -> None:
+        if getattr(self, "_host_ptr", None):
+            self.host = None
+            _check(load_library().engram_host_free(self._host_ptr))
+            self._host_ptr = None
+            self.device_ptr = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def _dense(t: torch.Tensor, name: str) -> torch.Tensor:
@@ -113,21 +161,25 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
-def lookup(table: torch.Tensor, hash_ids: torch.Tensor, rows_out: torch.Tensor | None = None,
-           err_flag: torch.Tensor | None = None) -> torch.Tensor:
-    """rows[t, c, :] = table[hash_ids[t, c], :] (hash_ids may be strided)."""
+def lookup(table, hash_ids: torch.Tensor, rows_out: torch.Tensor | None = None,
+           err_flag: torch.Tensor | None = None, background: bool = False) -> torch.Tensor:
+    """rows[t, c, :] = table[hash_ids[t, c], :] (hash_ids may be strided).
+    ``table`` is a device tensor or a HostTable; ``background`` selects
+    engram_lookup_background (half the grid, for a side stream)."""
     L = load_library()
-    _dense(table, "table")
+    if not isinstance(table, HostTable):
+        _dense(table, "table")
     T, C = hash_ids.shape
     hd = table.shape[1]
     if hash_ids.dtype != torch.int32:
         raise ValueError("hash_ids must be int32")
     if rows_out is None:
-        rows_out = torch.empty((T, C, hd), dtype=table.dtype, device=table.device)
+        rows_out = torch.empty((T, C, hd), dtype=table.dtype, device=hash_ids.device)
     _dense(rows_out, "rows_out")
-    _check(L.engram_lookup(_ptr(table), table.shape[0], hd, _ptr(hash_ids),
-                           hash_ids.stride(0), hash_ids.stride(1), T, C,
-                           _ptr(rows_out), _ptr(err_flag), _stream()))
+    fn = L.engram_lookup_background if background else L.engram_lookup
+    _check(fn(_ptr(table), table.shape[0], hd, _ptr(hash_ids),
+              hash_ids.stride(0), hash_ids.stride(1), T, C,
+              _ptr(rows_out), _ptr(err_flag), _stream()))
     return rows_out
 
 
@@ -290,7 +342,8 @@ def forward(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask
     L = load_library()
     for t, n in ((table, "table"), (w, "w"), (hidden, "hidden"),
                  (q_weight, "q_weight"), (k_weight, "k_weight")):
-        _dense(t, n)
+        if not isinstance(t, HostTable):
+            _dense(t, n)
     if out is None:
         out = torch.empty_like(hidden)
     args = forward_args(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask,
@@ -313,7 +366,8 @@ def forward_noalloc(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, to
     L = load_library()
     for t, n in ((table, "table"), (w, "w"), (hidden, "hidden"),
                  (q_weight, "q_weight"), (k_weight, "k_weight")):
-        _dense(t, n)
+        if not isinstance(t, HostTable):
+            _dense(t, n)
     if out is None:
         out = torch.empty_like(hidden)
     args = forward_args(table, hash_ids, w, w_scales, hidden, q_weight, k_weight, token_mask,
@@ -340,7 +394,8 @@ class ForwardPlan:
         L = load_library()
         for t, n in ((table, "table"), (w, "w"), (hidden, "hidden"),
                      (q_weight, "q_weight"), (k_weight, "k_weight")):
-            _dense(t, n)
+            if not isinstance(t, HostTable):
+                _dense(t, n)
         if out is None:
             out = torch.empty_like(hidden)
         self.out = out

@@ -81,6 +81,43 @@ int engram_lookup(const void* table, int64_t num_rows, int32_t head_dim,
                   void* rows_out, int32_t* err_flag, void* stream);
 
 /*
+ * engram_lookup_background -- engram_lookup for a side stream.
+ *   [P-common] ParallelEngramEmbedding.lookup: with `background` set the
+ *   persistent grid is halved so that the lookup leaves compute units to the
+ *   kernels of the main stream; Engram.prepare_embeddings issues the layer's
+ *   lookup ahead of its forward. Here the grid is capped at half the compute
+ *   units (one workgroup of 256 threads per two CUs; engram_lookup runs up to
+ *   8 per CU). Same arguments, results (bit for bit), error flag and errors
+ *   as engram_lookup. Enqueue it on a stream other than the one whose work it
+ *   should overlap (both at the default priority), and order the consumer
+ *   after it with an event.
+ */
+int engram_lookup_background(const void* table, int64_t num_rows, int32_t head_dim,
+                             const int32_t* hash_ids, int64_t ids_stride_t,
+                             int64_t ids_stride_c, int64_t T, int32_t n_cols,
+                             void* rows_out, int32_t* err_flag, void* stream);
+
+/*
+ * Host-resident tables.
+ *   [P-common] ParallelEngramEmbedding (docstring: with cpu_offload the
+ *   table shard lives in pinned host memory and is read over UVA;
+ *   _storage). engram_host_alloc returns page-locked host memory mapped into
+ *   the device's address space (hipHostMalloc, mapped and portable):
+ *     *host_ptr    the address the CPU writes the table through;
+ *     *device_ptr  the address kernels read it through: pass it as `table`
+ *                  to engram_lookup, engram_lookup_background or
+ *                  engram_forward, whose gathers then read the rows over the
+ *                  host link (results bit for bit those of a device table).
+ *   The memory is the caller's until engram_host_free(host_ptr); it is not
+ *   a device allocation and is never touched by the library otherwise.
+ *   ENGRAM_EINVAL for bytes == 0 or NULL out-pointers, ENGRAM_EHIP when the
+ *   runtime cannot allocate or map it (both out-pointers are then NULL).
+ *   engram_host_free(NULL) is a no-op.
+ */
+int engram_host_alloc(size_t bytes, void** host_ptr, void** device_ptr);
+int engram_host_free(void* host_ptr);
+
+/*
  * engram_lookup_fp8 -- the row gather from an fp8 table, dequantized to bf16.
  *   [P-common] ParallelEngramEmbedding (docstring, __init__, lookup): the
  *   table is float8_e4m3fn [rows, dim] with one uint8 ue8m0 scale per row and

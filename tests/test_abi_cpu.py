@@ -133,6 +133,20 @@ def test_validation_answers_before_any_launch(lib):
     assert lib.engram_probe_stream(P, 0x2000, 24, 1, None) == 1    # not a multiple of 16
 
 
+def test_host_alloc_validation(lib):
+    """engram_host_alloc refuses a zero size and NULL out-pointers before
+    touching the runtime; engram_host_free(NULL) is a no-op."""
+    h, d = ctypes.c_void_p(), ctypes.c_void_p()
+    assert lib.engram_host_alloc(0, ctypes.byref(h), ctypes.byref(d)) == 1
+    assert lib.engram_host_alloc(4096, None, ctypes.byref(d)) == 1
+    assert lib.engram_host_alloc(4096, ctypes.byref(h), None) == 1
+    assert lib.engram_host_free(None) == 0
+    # the background lookup validates like engram_lookup
+    assert lib.engram_lookup_background(None, 10, 128, None, 16, 1, 0, 16, None, None, None) == 0
+    assert lib.engram_lookup_background(None, 10, 12, None, 16, 1, 4, 16, None, None, None) == 2
+    assert lib.engram_lookup_background(None, 10, 128, None, 16, 1, 4, 16, None, None, None) == 1
+
+
 def test_workspace_sizes(lib):
     from gram_memory_layer_engram_amd import engram
 

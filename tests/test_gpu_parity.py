@@ -175,6 +175,133 @@ def test_lookup_strided_ids_and_bad_ids():
     assert np.array_equal(bits(rows), want)
 
 
+@pytest.mark.parametrize("name", ["tiny", "prefill", "decode_t16", "long"])
+def test_lookup_background_bit_exact(name):
+    """engram_lookup_background on a side stream (half the persistent grid,
+    so each workgroup walks more pieces): the rows of engram_lookup bit for
+    bit, and the oracle's rows on sampled tokens."""
+    E = _E()
+    inp = inputs(name)
+    wl = inp["wl"]
+    _say(f"background lookup {name} T={wl.T}")
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(main)
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    with torch.cuda.stream(side):
+        rows_bg = E.lookup(inp["table"], inp["ids"], err_flag=err, background=True)
+    main.wait_stream(side)
+    rows = E.lookup(inp["table"], inp["ids"])
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert torch.equal(rows_bg.view(torch.int16), rows.view(torch.int16))
+    toks = sample_tokens(wl.T, 4096 if wl.T > 4096 else wl.T, seed=12)
+    assert np.array_equal(bits(rows_bg)[toks], host_rows(inp, toks))
+
+
+def test_lookup_background_bad_ids_and_strides():
+    E = _E()
+    inp = inputs("tiny")
+    wl = inp["wl"]
+    three = torch.zeros((wl.T, 3, wl.C), dtype=torch.int32, device=DEV)
+    three[:, 2, :] = inp["ids"]
+    view = three[:, 2, :].clone()
+    view[5, 1] = W.num_rows(wl) + 3
+    view[9, 4] = -1
+    three[:, 2, :] = view
+    err = torch.zeros(1, dtype=torch.int32, device=DEV)
+    rows = E.lookup(inp["table"], three[:, 2, :], err_flag=err, background=True)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 1
+    want, flag = o.gather_rows(bits(inp["table"]), view.cpu().numpy())
+    assert flag
+    assert np.array_equal(bits(rows), want)
+
+
+def test_chunked_prefill_with_background_lookups():
+    """The use the background lookup is for: a chunked prefill whose next
+    chunk's rows are gathered on a side stream while the main stream runs
+    the current chunk's projection and gate (engram_wkv + engram_gate, the
+    kv-stored composition). Events order each chunk's projection after its
+    gather and each gather after the projection that last read its buffer
+    (two row buffers in turn). The output is the whole-batch
+    ENGRAM_FORWARD_STORE_KV forward's, bit for bit."""
+    E = _E()
+    inp = inputs("mid")
+    wl = inp["wl"]
+    chunks = 4
+    ct = wl.T // chunks
+    main = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    bufs = [torch.empty((ct, wl.C, wl.head_dim), dtype=torch.bfloat16, device=DEV) for _ in range(2)]
+    kv = torch.empty((ct, wl.N), dtype=torch.bfloat16, device=DEV)
+    out = torch.empty_like(inp["hidden"])
+    gathered = [torch.cuda.Event() for _ in range(chunks)]
+    consumed = [torch.cuda.Event() for _ in range(chunks)]
+    side.wait_stream(main)
+
+    def gather(c):
+        with torch.cuda.stream(side):
+            if c >= 2:
+                side.wait_event(consumed[c - 2])
+            E.lookup(inp["table"], inp["ids"][c * ct:(c + 1) * ct], rows_out=bufs[c % 2], background=True)
+            gathered[c].record(side)
+
+    gather(0)
+    for c in range(chunks):
+        if c + 1 < chunks:
+            gather(c + 1)
+        main.wait_event(gathered[c])
+        sl = slice(c * ct, (c + 1) * ct)
+        E.wkv(bufs[c % 2].view(ct, wl.K), inp["w"], kv=kv)
+        consumed[c].record(main)
+        E.gate(inp["hidden"][sl], kv, inp["q"], inp["k"], inp["mask"][sl], wl.eps, wl.clamp, out=out[sl])
+    ref = E.forward(inp["table"], inp["ids"], inp["w"], None, inp["hidden"], inp["q"], inp["k"], inp["mask"],
+                    wl.eps, wl.clamp, store_kv=True)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("wfmt,T", [("bf16", 64), ("bf16", 300), ("mxfp8", 16), ("mxfp8", 257)])
+def test_host_table_lookup_and_forward(wfmt, T):
+    """A table in page-locked host memory mapped into the device's address
+    space (engram_host_alloc): engram_lookup, engram_lookup_background and
+    engram_forward read its rows over the host link and give the device
+    table's results bit for bit (the rows also the oracle's)."""
+    E = _E()
+    g = torch.Generator(device=DEV).manual_seed(7300 + T)
+    R, C, hd, dim, hc = 50021, 8, 128, 256, 2
+    K, N = C * hd, (hc + 1) * dim
+    table = (torch.randn((R, hd), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    ids = torch.randint(0, R, (T, C), generator=g, device=DEV, dtype=torch.int32)
+    if wfmt == "bf16":
+        w = (torch.randn((N, K), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+        ws = None
+    else:
+        w = torch.randn((N, K), generator=g, device=DEV).to(torch.float8_e4m3fn).view(torch.uint8)
+        ws = (127 + torch.randint(-8, 1, (N // 32, K // 32), generator=g, device=DEV)).to(torch.uint8)
+    hidden = torch.randn((T, hc, dim), generator=g, device=DEV).to(torch.bfloat16)
+    q = (1 + 0.1 * torch.randn((hc, dim), generator=g, device=DEV)).to(torch.bfloat16)
+    k = (1 + 0.1 * torch.randn((hc, dim), generator=g, device=DEV)).to(torch.bfloat16)
+    mask = torch.rand((T,), generator=g, device=DEV) > 0.2
+    _say(f"host table {wfmt} T={T}")
+    ht = E.HostTable(R, hd).copy_from(table)
+    try:
+        rows_h = E.lookup(ht, ids)
+        rows_hb = E.lookup(ht, ids, background=True)
+        rows_d = E.lookup(table, ids)
+        out_h = E.forward(ht, ids, w, ws, hidden, q, k, mask)
+        out_d = E.forward(table, ids, w, ws, hidden, q, k, mask)
+        torch.cuda.synchronize()
+        assert torch.equal(rows_h.view(torch.int16), rows_d.view(torch.int16))
+        assert torch.equal(rows_hb.view(torch.int16), rows_d.view(torch.int16))
+        want, _ = o.gather_rows(bits(table), ids.cpu().numpy())
+        assert np.array_equal(bits(rows_h), want)
+        assert torch.equal(out_h.view(torch.int16), out_d.view(torch.int16))
+    finally:
+        ht.close()
+
+
 @pytest.mark.parametrize("hd", [8, 32, 64, 128, 96, 1024])
 @pytest.mark.parametrize("T", [1, 17, 65, 1000])
 def test_lookup_shapes(hd, T):
