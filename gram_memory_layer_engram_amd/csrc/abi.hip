@@ -262,6 +262,18 @@ int engram_wkv(const void* x, int64_t T, int32_t K, const void* w,
   return run_wkv(x, T, K, w, w_scales, w_format, N, kv, workspace, (hipStream_t)stream);
 }
 
+int engram_gate_finish(const void* hidden, const void* value, const float* partials,
+                       const uint8_t* token_mask, int64_t T, int32_t hc, int32_t dim, float eps,
+                       float clamp, void* out, float* gate_out, void* stream) {
+  int st = check_gate(hidden, value, value, value, T, hc, dim, out);
+  if (st != ENGRAM_OK) return st;
+  if (dim % 256 != 0) return ENGRAM_EUNSUPPORTED;
+  if (T == 0) return ENGRAM_OK;
+  if (!partials || ((uintptr_t)partials & 7u)) return ENGRAM_EINVAL;
+  return hip_status(launch_gate_parts(hidden, value, (const float2*)partials, token_mask, T, hc, dim, eps,
+                                      clamp, out, gate_out, (hipStream_t)stream));
+}
+
 int engram_gate(const void* hidden, const void* kv, const void* q_weight,
                 const void* k_weight, const uint8_t* token_mask, int64_t T,
                 int32_t hc, int32_t dim, float eps, float clamp, void* out,

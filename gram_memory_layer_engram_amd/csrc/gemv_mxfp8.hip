@@ -146,6 +146,159 @@ __global__ __launch_bounds__(GV_THREADS) void gemv_mxfp8_kernel(
   }
 }
 
+// The same GEMV for 2..4 token tiles with x staged in LDS. Holding all of
+// x's fragments in registers limited the row tiles per workgroup (RT*NT <= 8:
+// 640 workgroups at 64 tokens, each re-reading all of x, 84 MB of L2 reads for
+// a 42 MB weight); here each workgroup copies x (codes and scale bytes) into
+// LDS once with direct-to-LDS DMAs issued after its weight loads, so RT = 5
+// at any NT: 256 workgroups of 80 rows. LDS row R (a token) holds its k
+// pieces with piece p at p ^ (R & 15) inside each 256-byte run, so the 16 rows
+// a fragment read touches fall on distinct banks. After the MFMAs the same
+// LDS holds the waves' partial tiles for the fixed-order sum.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+template <int RT, int NT>
+constexpr int xlds_bytes(int K) {
+  const int x = NT * 16 * K + ((NT * 16 * (K / 32) + 1023) & ~1023);
+  const int red = GV_WAVES * RT * NT * 1024;
+  return x > red ? x : red;
+}
+
+template <int RT, int NT, int SPW>
+__global__ __launch_bounds__(GV_THREADS) void gemv_mxfp8_xlds_kernel(
+    const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, int T,
+    int K, const uint8_t* __restrict__ w, const uint8_t* __restrict__ ws,
+    int N, uint16_t* __restrict__ kv) {
+  extern __shared__ __attribute__((aligned(1024))) char lds[];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n0 = blockIdx.x * 16 * RT;
+  const int g = lane >> 4, r = lane & 15;
+  const int kb = K / 32;
+  const int nsteps = K / 128;
+  const int step0 = wave * SPW;
+  constexpr int ROWS = NT * 16;
+
+  uint4 wlo[RT][SPW], whi[RT][SPW];
+  int wsc[RT][SPW];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int nrow = n0 + rt * 16;
+    const uint8_t* wrow = w + (int64_t)(nrow + r) * K;
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+      wlo[rt][s] = whi[rt][s] = make_uint4(0, 0, 0, 0);
+      wsc[rt][s] = 0;
+      if (step0 + s < nsteps) {
+        const int kbyte = (step0 + s) * 128 + 16 * g;
+        wlo[rt][s] = *reinterpret_cast<const uint4*>(wrow + kbyte);
+        whi[rt][s] = *reinterpret_cast<const uint4*>(wrow + kbyte + 64);
+        wsc[rt][s] = ws[(nrow / 32) * kb + (step0 + s) * 4 + g];
+      }
+    }
+  }
+  // x -> LDS: instruction q writes LDS bytes [1024q, 1024q + 1024), lane l
+  // the 16 bytes at 1024q + 16l, i.e. row R, position p of that row; it
+  // fetches piece p ^ (R & 15) of token R (zeros past T: the range check)
+  {
+    const rsrc_t rx = make_rsrc(xq, (uint32_t)(T * K));
+    const rsrc_t rs = make_rsrc(xs, (uint32_t)(T * kb));
+    const int pieces_row = K / 16;
+    const int nq = ROWS * K / 1024;
+    for (int q = wave; q < nq; q += GV_WAVES) {
+      const int P = q * 64 + lane;             // LDS piece index
+      const int R = P / pieces_row, p = P - R * pieces_row;
+      const uint32_t voff = (uint32_t)R * (uint32_t)K + (uint32_t)((p ^ (R & 15)) * 16);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (lds_ptr_t)(lds + q * 1024), 16, voff, 0, 0, 0);
+    }
+    const int nqs = (ROWS * kb + 1023) / 1024;
+    for (int q = wave; q < nqs; q += GV_WAVES)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_ptr_t)(lds + ROWS * K + q * 1024), 16,
+                                               (uint32_t)(q * 1024 + lane * 16), 0, 0, 0);
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+
+  f32x4 acc[RT][NT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc[rt][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int j = 0; j < NT; ++j) {
+    const int R = j * 16 + r;
+    const char* xrow = lds + R * K;
+#pragma unroll
+    for (int s = 0; s < SPW; ++s) {
+      if (step0 + s >= nsteps) break;  // uniform per wave
+      const int P0 = (step0 + s) * 8 + g;     // the piece of k bytes 128*step + 16g; +4 is 64 bytes on
+      const uint4 lo = *reinterpret_cast<const uint4*>(xrow + ((P0 ^ (R & 15)) << 4));
+      const uint4 hi = *reinterpret_cast<const uint4*>(xrow + (((P0 + 4) ^ (R & 15)) << 4));
+      const int xsc = (int)(uint8_t)lds[ROWS * K + R * kb + (step0 + s) * 4 + g];
+      const i32x8 xb = cat(lo, hi);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+        acc[rt][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+            cat(wlo[rt][s], whi[rt][s]), xb, acc[rt][j], 0, 0, 0, wsc[rt][s], 0, xsc);
+    }
+  }
+
+  __syncthreads();   // every wave is done with x in LDS
+  f32x4* red = reinterpret_cast<f32x4*>(lds);
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int j = 0; j < NT; ++j) red[(wave * RT * NT + rt * NT + j) * 64 + lane] = acc[rt][j];
+  __syncthreads();
+  for (int idx = tid; idx < RT * NT * 64; idx += GV_THREADS) {
+    const int pair = idx >> 6, l = idx & 63;
+    const int rt = pair / NT, j = pair - rt * NT;
+    f32x4 sum = red[pair * 64 + l];
+#pragma unroll
+    for (int v = 1; v < GV_WAVES; ++v) {
+      const f32x4 pv = red[(v * RT * NT + pair) * 64 + l];
+      sum[0] += pv[0]; sum[1] += pv[1]; sum[2] += pv[2]; sum[3] += pv[3];
+    }
+    const int t = j * 16 + (l & 15);
+    if (t < T) {
+      const int n = n0 + rt * 16 + 4 * (l >> 4);
+      uint2 o;
+      o.x = pack_bf16x2(sum[0], sum[1]);
+      o.y = pack_bf16x2(sum[2], sum[3]);
+      *reinterpret_cast<uint2*>(kv + (int64_t)t * N + n) = o;
+    }
+  }
+}
+
+template <int RT, int NT>
+hipError_t gemv_xlds(const uint8_t* xq, const uint8_t* xs, int T, int K, const uint8_t* w, const uint8_t* ws,
+                     int N, void* kv, hipStream_t s) {
+  const int spw = (K / 128 + GV_WAVES - 1) / GV_WAVES;
+  const int lds = xlds_bytes<RT, NT>(K);
+  const dim3 grid(N / (16 * RT)), block(GV_THREADS);
+  hipError_t e;
+  switch (spw) {
+#define GX_CASE(S)                                                                                     \
+  case S:                                                                                              \
+    e = hipFuncSetAttribute((const void*)gemv_mxfp8_xlds_kernel<RT, NT, S>,                            \
+                            hipFuncAttributeMaxDynamicSharedMemorySize, lds);                          \
+    if (e != hipSuccess) return e;                                                                     \
+    hipLaunchKernelGGL((gemv_mxfp8_xlds_kernel<RT, NT, S>), grid, block, lds, s, xq, xs, T, K, w, ws, N, \
+                       (uint16_t*)kv);                                                                 \
+    break;
+    GX_CASE(1) GX_CASE(2)
+#undef GX_CASE
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <int RT, int NT>
 hipError_t gemv_rt(const uint8_t* xq, const uint8_t* xs, int T, int K,
                    const uint8_t* w, const uint8_t* ws, int N, void* kv,
@@ -172,6 +325,12 @@ hipError_t gemv_nt(const uint8_t* xq, const uint8_t* xs, int T, int K,
                    const uint8_t* w, const uint8_t* ws, int N, void* kv,
                    hipStream_t s) {
   const int tiles = N / 16;
+  // two or more token tiles: x in LDS when it fits (K % 256 == 0 for the
+  // swizzle, at most 2 k steps per wave)
+  if constexpr (NT >= 2) {
+    if (tiles % 5 == 0 && K % 256 == 0 && K / 128 <= 2 * GV_WAVES && xlds_bytes<5, NT>(K) <= 160 * 1024)
+      return gemv_xlds<5, NT>(xq, xs, T, K, w, ws, N, kv, s);
+  }
   if constexpr (5 * NT <= 8)
     if (tiles % 5 == 0) return gemv_rt<5, NT>(xq, xs, T, K, w, ws, N, kv, s);
   if constexpr (4 * NT <= 8)

@@ -57,6 +57,7 @@ EXPORTS = {
     "engram_wkv_gate_partials": (_i32, [_vp, _i64, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp,
                                         _vp, _sz, _vp]),
     "engram_gate": (_i32, [_vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _f32, _f32, _vp, _vp, _vp]),
+    "engram_gate_finish": (_i32, [_vp, _vp, _vp, _vp, _i64, _i32, _i32, _f32, _f32, _vp, _vp, _vp]),
     "engram_forward_workspace_size": (_sz, [ctypes.POINTER(ForwardArgs)]),
     "engram_forward": (_i32, [ctypes.POINTER(ForwardArgs), _vp, _sz, _vp]),
     "engram_forward_single_launch": (_i32, [ctypes.POINTER(ForwardArgs), _vp, _sz, _vp]),
@@ -283,6 +284,23 @@ def wkv_gate_partials(x: torch.Tensor, w: torch.Tensor, w_scales: torch.Tensor |
                                       _ptr(q_weight), _ptr(k_weight), _ptr(value), _ptr(partials),
                                       _ptr(workspace), ws_bytes, _stream()))
     return value, partials
+
+
+def gate_finish(hidden: torch.Tensor, value: torch.Tensor, partials: torch.Tensor,
+                token_mask: torch.Tensor | None = None, eps: float = 1e-6, clamp: float = 1e-6,
+                out: torch.Tensor | None = None, gate_out: torch.Tensor | None = None) -> torch.Tensor:
+    """The gate and update from wkv_gate_partials' value and partials."""
+    L = load_library()
+    for t, n in ((hidden, "hidden"), (value, "value"), (partials, "partials")):
+        _dense(t, n)
+    T, hc, dim = hidden.shape
+    if tuple(partials.shape) != (hc, T, max(1, dim // 256), 2) or partials.dtype != torch.float32:
+        raise ValueError(f"partials must be fp32 [{hc}, {T}, {dim // 256}, 2]")
+    if out is None:
+        out = torch.empty_like(hidden)
+    _check(L.engram_gate_finish(_ptr(hidden), _ptr(value), _ptr(partials), _ptr(token_mask), T, hc, dim,
+                                eps, clamp, _ptr(out), _ptr(gate_out), _stream()))
+    return out
 
 
 def gate(hidden: torch.Tensor, kv: torch.Tensor, q_weight: torch.Tensor, k_weight: torch.Tensor,

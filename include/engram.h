@@ -194,7 +194,7 @@ int engram_wkv(const void* x, int64_t T, int32_t K, const void* w,
  *     partials[2*((h*T + t)*(dim/256) + i) + 1] = sum key^2
  *   over the tile, on the bf16-rounded keys (fp32, fixed order). The keys
  *   never reach memory. engram_forward uses it where it applies and finishes
- *   the gate from the partials.
+ *   the gate from the partials (engram_gate_finish).
  *
  *   x, T, K, w, w_scales, w_format: as engram_wkv, with N = (hc+1)*dim.
  *   hidden      bf16 [T, hc, dim];  q_weight, k_weight  bf16 [hc, dim]
@@ -212,6 +212,30 @@ int engram_wkv_gate_partials(const void* x, int64_t T, int32_t K, const void* w,
                              int32_t dim, const void* hidden, const void* q_weight,
                              const void* k_weight, void* value, float* partials,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * engram_gate_finish -- the gate and residual update from per-tile partials.
+ *   [P-rocm] _engram_gate_finish_kernel: the finish step of the partial /
+ *   finish split, here with the partials of engram_wkv_gate_partials (one
+ *   shard = one 256-column tile). For every token t and copy h:
+ *     dot, ks = sums over the dim/256 tiles i of partials[h, t, i, 0] and
+ *               partials[h, t, i, 1]
+ *     hs  = sum hidden[t,h,:]^2
+ *     g   = sigmoid(sign(d) * sqrt(max(|d|, clamp))),
+ *           d = dot * rsqrt(hs/dim + eps) * rsqrt(ks/dim + eps) * rsqrt(dim)
+ *     out[t,h,:] = bf16(hidden[t,h,:] + g * value[t,:])
+ *   Tokens whose mask byte is 0 pass through: out = hidden bit for bit, g = 0.
+ *
+ *   hidden      bf16 [T, hc, dim];  value  bf16 [T, dim]
+ *   partials    fp32 [hc, T, dim/256, 2] as engram_wkv_gate_partials writes
+ *               them, 8-byte aligned
+ *   token_mask, out, gate_out  as engram_gate. All sums in fp32 in a fixed
+ *   order. Shapes: dim % 256 == 0, dim <= 16384, 1 <= hc <= 8; else
+ *   ENGRAM_EUNSUPPORTED.
+ */
+int engram_gate_finish(const void* hidden, const void* value, const float* partials,
+                       const uint8_t* token_mask, int64_t T, int32_t hc, int32_t dim,
+                       float eps, float clamp, void* out, float* gate_out, void* stream);
 
 /*
  * engram_gate -- gate and residual update.

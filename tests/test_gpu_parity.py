@@ -984,6 +984,69 @@ def test_wkv_gate_partials_against_oracle_partials(wfmt, T, dim, hc, K):
             assert np.all(np.abs(p[:, :, i, 1].T - ks_ref) <= 2e-2 * ks_ref + 1e-6), i
 
 
+@pytest.mark.parametrize("hc,dim,T", [(4, 4096, 300), (1, 256, 1), (3, 768, 65), (8, 512, 17), (2, 16384, 9),
+                                      (5, 1280, 130)])
+def test_gate_finish_against_oracle_shard_route(hc, dim, T):
+    """engram_gate_finish on partials the oracle's shard route forms from a
+    given kv (one shard per 256 columns: sum key^2 and sum hidden*q*k*key
+    from gate_partials): the gate within
+    1e-3 of the oracle's gate_finish, >= 99.9% of the outputs its bf16 or one
+    step away, masked rows hidden bit for bit with gate 0."""
+    E = _E()
+    g = torch.Generator(device=DEV).manual_seed(9400 + hc * 31 + dim + T)
+    hidden = torch.randn((T, hc, dim), generator=g, device=DEV).to(torch.bfloat16)
+    kv = (torch.randn((T, (hc + 1) * dim), generator=g, device=DEV) * 0.3).to(torch.bfloat16)
+    q = (1 + 0.1 * torch.randn((hc, dim), generator=g, device=DEV)).to(torch.bfloat16)
+    k = (1 + 0.1 * torch.randn((hc, dim), generator=g, device=DEV)).to(torch.bfloat16)
+    mask = torch.rand((T,), generator=g, device=DEV) > 0.25
+    hb, kvb, qb, kb = bits(hidden), bits(kv), bits(q), bits(k)
+    tiles = dim // 256
+    part = np.zeros((hc, T, tiles, 2), np.float32)
+    shards = []
+    for i in range(tiles):
+        cols = np.concatenate([np.arange(h * dim + 256 * i, h * dim + 256 * i + 256) for h in range(hc)]
+                              + [np.arange(hc * dim + 256 * i, hc * dim + 256 * i + 256)])
+        ks_i, dot_i, val_i = o.gate_partials(hb, kvb[:, cols], qb, kb, 256 * i)
+        shards.append((ks_i, dot_i, val_i))
+        part[:, :, i, 0] = dot_i.T
+        part[:, :, i, 1] = ks_i.T
+    value = kv[:, hc * dim:].contiguous()
+    gate_out = torch.empty((T, hc), dtype=torch.float32, device=DEV)
+    out = E.gate_finish(hidden, value, torch.from_numpy(part).to(DEV), mask, 1e-6, 1e-6, gate_out=gate_out)
+    torch.cuda.synchronize()
+    m = mask.cpu().numpy()
+    ref_out, ref_g = o.gate_finish(hb, shards, m, 1e-6, 1e-6)
+    ref_out = np.where(m[:, None, None], ref_out, hb)
+    assert np.max(np.abs(gate_out.cpu().numpy() - ref_g)) <= GATE_ABS
+    assert np.mean(ulp_distance_bf16(bits(out), ref_out) <= 1) >= 0.999
+    assert np.array_equal(bits(out)[~m], hb[~m])
+    assert np.all(gate_out.cpu().numpy()[~m] == 0)
+
+
+@pytest.mark.parametrize("wfmt,T,dim,hc", [("bf16", 300, 512, 3), ("mxfp8", 257, 1024, 2)])
+def test_partials_then_finish_is_the_default_forward(wfmt, T, dim, hc):
+    """engram_wkv_gate_partials followed by engram_gate_finish on the
+    gathered rows gives the default forward's output and gates bit for bit
+    (the same kernels in the same order)."""
+    E = _E()
+    c = _decode_case(T, dim, hc, seed=9500 + T, C=4)
+    if wfmt == "bf16":
+        g = torch.Generator(device=DEV).manual_seed(9600 + T)
+        K, N = 4 * 128, (hc + 1) * dim
+        c["w"] = (torch.randn((N, K), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+        c["ws"] = None
+    g_fwd = torch.empty((T, hc), dtype=torch.float32, device=DEV)
+    out = E.forward(c["table"], c["ids"], c["w"], c["ws"], c["hidden"], c["q"], c["k"], c["mask"],
+                    gate_out=g_fwd)
+    x = E.lookup(c["table"], c["ids"]).view(T, -1)
+    value, part = E.wkv_gate_partials(x, c["w"], c["ws"], c["hidden"], c["q"], c["k"])
+    g_two = torch.empty((T, hc), dtype=torch.float32, device=DEV)
+    out2 = E.gate_finish(c["hidden"], value, part, c["mask"], gate_out=g_two)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(g_fwd, g_two)
+
+
 @pytest.mark.parametrize("C", [4, 3])
 @pytest.mark.parametrize("T", [1, 5, 16, 17, 31, 32, 33, 64, 65])
 def test_forward_mxfp8_decode_paths_and_bad_ids(T, C):
