@@ -1,0 +1,44 @@
+"""The C ABI's argument checks under AddressSanitizer (CPU only).
+
+csrc/abi.hip is compiled with AddressSanitizer on its host side (the device
+side is built as usual: sanitizers apply to host code only), linked with
+tests/abi_asan_driver.c and the built library, and run: every entry point is
+called with bad, edge and empty arguments that the checks answer before any
+launch, so no GPU is needed, and any out-of-bounds or use-after-free access
+in the validation or workspace arithmetic aborts the run.
+"""
+
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+PKG = os.path.join(ROOT, "gram_memory_layer_engram_amd")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+
+def test_abi_checks_under_asan(tmp_path):
+    lib = os.path.join(PKG, "libengram.so")
+    if not os.path.exists(lib):
+        pytest.skip("libengram.so is not built")
+    if not os.path.exists(HIPCC) or shutil.which("gcc") is None:
+        pytest.skip("no hipcc / gcc")
+    abi_o = tmp_path / "abi_asan.o"
+    drv_o = tmp_path / "drv.o"
+    exe = tmp_path / "abi_asan"
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-O1", "-fPIC", "-std=c++17", "-g",
+                    "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer",
+                    "-Wno-unused-result", "-c", os.path.join(PKG, "csrc", "abi.hip"), "-o", str(abi_o)],
+                   check=True, capture_output=True)
+    subprocess.run(["gcc", "-std=c11", "-g", "-c", os.path.join(ROOT, "tests", "abi_asan_driver.c"),
+                    "-o", str(drv_o)], check=True, capture_output=True)
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-Xarch_host", "-fsanitize=address", str(drv_o), str(abi_o), lib,
+                    f"-Wl,-rpath,{PKG}", "-o", str(exe)], check=True, capture_output=True)
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1")
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120, env=env)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert " 0 failures" in r.stdout, r.stdout
