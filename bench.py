@@ -13,8 +13,10 @@ measured afterwards.
 Prints one JSON line. ``value`` is prefill tokens/s. ``roofline`` is the
 dominant kernel (the wkv GEMM with the gate epilogue that the default
 forward launches, MFMA-bound), its duration taken from HIP events on the
-launch stream around calls of engram_wkv_gate_partials in the same launch
-configuration. ``configs`` has one row per workload the layer is specified
+launch stream around engram_wkv_gate_partials, called between the
+forward's other two launches (engram_lookup before it, engram_gate_finish
+after it: the forward's own kernels in its order, so the GEMM runs in the
+cache and clock state the forward gives it). ``configs`` has one row per workload the layer is specified
 on (tiny, mid, prefill, decode at T = 1, 4, 16, 64, long): forward time,
 tokens/s, the bound and the fraction of that bound's peak. The decode rows
 are measured cold: 16 copies of the 40 MiB weight are rotated so no step
@@ -111,7 +113,7 @@ def _plan(E, inp, wl, out, **kw):
                          inp["k"], inp["mask"], wl.eps, wl.clamp, out=out, **kw)
 
 
-def bench_prefill(steps, warmup):
+def bench_prefill(steps, warmup, offload=True):
     """The headline: W warm-up forwards, then K timed forwards; afterwards
     the per-kernel durations of the same step."""
     import torch
@@ -147,7 +149,6 @@ def bench_prefill(steps, warmup):
     ids = inp["ids"]
     look = (inp["table"].data_ptr(), inp["table"].shape[0], wl.head_dim, ids.data_ptr(), ids.stride(0),
             ids.stride(1), wl.T, wl.C, rows.data_ptr(), None, sp)
-    t_lookup = _events_time(lambda i: L.engram_lookup(*look), n, stream)
     value = torch.empty((wl.T, wl.dim), dtype=torch.bfloat16, device="cuda")
     parts = torch.empty((wl.hc, wl.T, wl.dim // 256, 2), dtype=torch.float32, device="cuda")
     fused = (x.data_ptr(), wl.T, wl.K, inp["w"].data_ptr(), None, E.W_BF16, wl.hc, wl.dim,
@@ -155,14 +156,36 @@ def bench_prefill(steps, warmup):
              parts.data_ptr(), None, 0, sp)
     if L.engram_wkv_gate_partials(*fused) != 0:
         raise RuntimeError("engram_wkv_gate_partials refused the prefill shapes")
-    t_fused = _events_time(lambda i: L.engram_wkv_gate_partials(*fused), n, stream)
+    finish = (inp["hidden"].data_ptr(), value.data_ptr(), parts.data_ptr(), None, wl.T, wl.hc, wl.dim, wl.eps,
+              wl.clamp, out.data_ptr(), None, sp)
+    # the default forward's three launches as separate C calls in the same
+    # order (the same kernels, bit for bit the forward's output), an event
+    # between each: every kernel is timed in the cache and clock state the
+    # forward gives it (the projection GEMM runs ~5% slower there than
+    # back to back, after the finish kernel's 580 MB of traffic)
+    t_lookup, t_fused, t_finish = [], [], []
+    for _ in range(n):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        ev[0].record(stream)
+        L.engram_lookup(*look)
+        ev[1].record(stream)
+        L.engram_wkv_gate_partials(*fused)
+        ev[2].record(stream)
+        L.engram_gate_finish(*finish)
+        ev[3].record(stream)
+        torch.cuda.synchronize()
+        t_lookup.append(ev[0].elapsed_time(ev[1]))
+        t_fused.append(ev[1].elapsed_time(ev[2]))
+        t_finish.append(ev[2].elapsed_time(ev[3]))
+    # the same GEMM launched back to back (W and x stay in the caches)
+    t_fused_alone = _events_time(lambda i: L.engram_wkv_gate_partials(*fused), n, stream)
     wkv = (x.data_ptr(), wl.T, wl.K, inp["w"].data_ptr(), None, E.W_BF16, wl.N, kv.data_ptr(), None, 0, sp)
     t_wkv = _events_time(lambda i: L.engram_wkv(*wkv), n, stream)
     gate = (inp["hidden"].data_ptr(), kv.data_ptr(), inp["q"].data_ptr(), inp["k"].data_ptr(), None, wl.T,
             wl.hc, wl.dim, wl.eps, wl.clamp, out.data_ptr(), None, sp)
     t_gate = _events_time(lambda i: L.engram_gate(*gate), n, stream)
 
-    offload = bench_background_and_host_table(E, inp, wl)
+    offload = bench_background_and_host_table(E, inp, wl) if offload else None
 
     # the same gather from the table stored as fp8 (e4m3 + ue8m0 per 32), dequantized on lookup
     del plan, plan_kv, inp["table"]
@@ -176,6 +199,7 @@ def bench_prefill(steps, warmup):
     del codes, scales, inp
     torch.cuda.empty_cache()
     return wl, dt, {"lookup": t_lookup, "wkv_gate_partials": t_fused, "wkv": t_wkv, "gate": t_gate,
+                    "gate_finish": t_finish, "wkv_gate_partials_alone": t_fused_alone,
                     "lookup_fp8": t_lookup8, "forward": t_fwd, "forward_store_kv": t_fwd_kv}, offload
 
 
@@ -530,14 +554,14 @@ def main():
         print(json.dumps(bench_background_and_host_table(E, inp, wl, reps=5)), flush=True)
         return
 
-    wl, dt, kt, offload = bench_prefill(a.steps, a.warmup)
+    wl, dt, kt, offload = bench_prefill(a.steps, a.warmup, offload=not a.headline_only)
     avg = {k: statistics.fmean(v) for k, v in kt.items()}
     flops = 2.0 * wl.T * wl.K * wl.N
     fused_s = avg["wkv_gate_partials"] * 1e-3
     achieved = flops / fused_s / 1e12
     roofline = {
-        "kernel": "gemm_bf16_kernel with the gate epilogue (engram_wkv_gate_partials, the default "
-                  "forward's projection: 8192 x 20480 x 2048)",
+        "kernel": "gemm_bf16_kernel with the gate epilogue (the default forward's projection, 8192 x 20480 x "
+                  "2048), timed between the forward's lookup and finish launches",
         "bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
         "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
         "traffic": _traffic("gemm_bf16_kernel_gate_epilogue", "gram_memory_layer_engram_amd/csrc/gemm.hip"),
@@ -558,6 +582,12 @@ def main():
         "wkv_gate_partials_us": round(avg["wkv_gate_partials"] * 1e3, 2),
         "wkv_gate_partials_us_med_p10_p90": _us(kt["wkv_gate_partials"]),
         "wkv_gate_partials_mfma_frac": roofline["frac"],
+        "wkv_gate_partials_back_to_back_us": round(avg["wkv_gate_partials_alone"] * 1e3, 2),
+        "wkv_gate_partials_back_to_back_mfma_frac": round(flops / (avg["wkv_gate_partials_alone"] * 1e-3) / 1e12
+                                                          / BF16_PEAK_TFLOPS, 4),
+        "gate_finish_us": round(avg["gate_finish"] * 1e3, 2),
+        "gate_finish_hbm_frac": round(wl.T * (2 * wl.hc * wl.dim * 2 + wl.dim * 2 + wl.hc * (wl.dim // 256) * 8)
+                                      / (avg["gate_finish"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "wkv_us": round(avg["wkv"] * 1e3, 2),
         "wkv_us_med_p10_p90": _us(kt["wkv"]),
         "wkv_mfma_frac": round(flops / (avg["wkv"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
