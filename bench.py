@@ -203,28 +203,29 @@ def bench_prefill(steps, warmup, offload=True):
                     "lookup_fp8": t_lookup8, "forward": t_fwd, "forward_store_kv": t_fwd_kv}, offload
 
 
-def chunked_prefill(E, inp, wl, chunks, background, out, bufs, kv, main, side):
+def chunked_prefill(L, calls, chunks, background, main, side):
     """One prefill forward as `chunks` token chunks in the kv-stored
-    composition (lookup -> engram_wkv -> engram_gate). background: chunk
-    c+1's lookup runs on `side` with engram_lookup_background while `main`
-    runs chunk c's projection and gate (events order each projection after
-    its gather, each gather after the projection that last read its row
+    composition (lookup -> engram_wkv -> engram_gate), each call through
+    pre-marshalled C arguments (`calls[c]` = the chunk's three argument
+    tuples, the stream slot last and filled here). background: chunk c+1's
+    lookup runs on `side` with engram_lookup_background while `main` runs
+    chunk c's projection and gate (events order each projection after its
+    gather, each gather after the projection that last read its row
     buffer); else every step runs on `main` in order."""
     import torch
 
-    ct = wl.T // chunks
     gathered = [torch.cuda.Event() for _ in range(chunks)]
     consumed = [torch.cuda.Event() for _ in range(chunks)]
+    sm, ss = main.cuda_stream, side.cuda_stream
 
     def gather(c):
         if not background:
-            E.lookup(inp["table"], inp["ids"][c * ct:(c + 1) * ct], rows_out=bufs[c % 2])
+            L.engram_lookup(*calls[c][0], sm)
             return
-        with torch.cuda.stream(side):
-            if c >= 2:
-                side.wait_event(consumed[c - 2])
-            E.lookup(inp["table"], inp["ids"][c * ct:(c + 1) * ct], rows_out=bufs[c % 2], background=True)
-            gathered[c].record(side)
+        if c >= 2:
+            side.wait_event(consumed[c - 2])
+        L.engram_lookup_background(*calls[c][0], ss)
+        gathered[c].record(side)
 
     if background:
         side.wait_stream(main)
@@ -236,12 +237,10 @@ def chunked_prefill(E, inp, wl, chunks, background, out, bufs, kv, main, side):
             main.wait_event(gathered[c])
         else:
             gather(c)
-        sl = slice(c * ct, (c + 1) * ct)
-        E.wkv(bufs[c % 2].view(ct, wl.K), inp["w"], kv=kv)
+        L.engram_wkv(*calls[c][1], sm)
         if background:
             consumed[c].record(main)
-        E.gate(inp["hidden"][sl], kv, inp["q"], inp["k"], None if inp["mask"] is None else inp["mask"][sl],
-               wl.eps, wl.clamp, out=out[sl])
+        L.engram_gate(*calls[c][2], sm)
 
 
 def bench_background_and_host_table(E, inp, wl, reps=10, chunks=4):
@@ -250,23 +249,36 @@ def bench_background_and_host_table(E, inp, wl, reps=10, chunks=4):
     the same chunks run in order on one stream (wall time per forward);
     (b) the table in page-locked host memory, read over the host link by
     the same gather: the prefill lookup (Zipf ids) and a decode-size one
-    (the first 16 tokens), with the link's achieved rate."""
+    (16 tokens of uniform ids), beside the same gathers from the device
+    table."""
     import torch
 
+    L = E.load_library()
     main = torch.cuda.current_stream()
     side = torch.cuda.Stream()
     ct = wl.T // chunks
     bufs = [torch.empty((ct, wl.C, wl.head_dim), dtype=torch.bfloat16, device="cuda") for _ in range(2)]
     kv = torch.empty((ct, wl.N), dtype=torch.bfloat16, device="cuda")
     out = torch.empty_like(inp["hidden"])
+    tbl, ids, hid = inp["table"], inp["ids"], inp["hidden"]
+    calls = []
+    for c in range(chunks):
+        t0 = c * ct
+        rows = bufs[c % 2]
+        calls.append((
+            (tbl.data_ptr(), tbl.shape[0], wl.head_dim, ids[t0].data_ptr(), ids.stride(0), ids.stride(1), ct, wl.C,
+             rows.data_ptr(), None),
+            (rows.data_ptr(), ct, wl.K, inp["w"].data_ptr(), None, E.W_BF16, wl.N, kv.data_ptr(), None, 0),
+            (hid[t0].data_ptr(), kv.data_ptr(), inp["q"].data_ptr(), inp["k"].data_ptr(), None, ct, wl.hc, wl.dim,
+             wl.eps, wl.clamp, out[t0].data_ptr(), None)))
     res = {}
     for bg in (False, True):
         for _ in range(2):
-            chunked_prefill(E, inp, wl, chunks, bg, out, bufs, kv, main, side)
+            chunked_prefill(L, calls, chunks, bg, main, side)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(reps):
-            chunked_prefill(E, inp, wl, chunks, bg, out, bufs, kv, main, side)
+            chunked_prefill(L, calls, chunks, bg, main, side)
         torch.cuda.synchronize()
         res["chunked_background_us" if bg else "chunked_serial_us"] = round((time.perf_counter() - t0) / reps * 1e6, 1)
     del bufs, kv, out

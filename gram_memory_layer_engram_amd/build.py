@@ -39,7 +39,9 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
+    # only the C ABI (engram_*) is exported; the launchers and helpers stay local
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs,
+           f"-Wl,--version-script={os.path.join(CSRC, 'exports.map')}", "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")

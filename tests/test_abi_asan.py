@@ -2,7 +2,8 @@
 
 csrc/abi.hip is compiled with AddressSanitizer on its host side (the device
 side is built as usual: sanitizers apply to host code only), linked with
-tests/abi_asan_driver.c and the built library, and run: every entry point is
+tests/abi_asan_driver.c and the library's other objects from the in-tree
+build, and run: every entry point is
 called with bad, edge and empty arguments that the checks answer before any
 launch, so no GPU is needed, and any out-of-bounds or use-after-free access
 in the validation or workspace arithmetic aborts the run.
@@ -21,10 +22,13 @@ PKG = os.path.join(ROOT, "gram_memory_layer_engram_amd")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
+OTHERS = ["lookup", "gate", "mxq", "gemm", "gemv_mxfp8", "decode_forward", "probe"]
+
+
 def test_abi_checks_under_asan(tmp_path):
-    lib = os.path.join(PKG, "libengram.so")
-    if not os.path.exists(lib):
-        pytest.skip("libengram.so is not built")
+    objs = [os.path.join(PKG, "_build", f"{n}.o") for n in OTHERS]
+    if not all(os.path.exists(o) for o in objs):
+        pytest.skip("the library's objects are not built (python -m gram_memory_layer_engram_amd.build)")
     if not os.path.exists(HIPCC) or shutil.which("gcc") is None:
         pytest.skip("no hipcc / gcc")
     abi_o = tmp_path / "abi_asan.o"
@@ -36,8 +40,8 @@ def test_abi_checks_under_asan(tmp_path):
                    check=True, capture_output=True)
     subprocess.run(["gcc", "-std=c11", "-g", "-c", os.path.join(ROOT, "tests", "abi_asan_driver.c"),
                     "-o", str(drv_o)], check=True, capture_output=True)
-    subprocess.run([HIPCC, "--offload-arch=gfx950", "-Xarch_host", "-fsanitize=address", str(drv_o), str(abi_o), lib,
-                    f"-Wl,-rpath,{PKG}", "-o", str(exe)], check=True, capture_output=True)
+    subprocess.run([HIPCC, "--offload-arch=gfx950", "-Xarch_host", "-fsanitize=address", str(drv_o), str(abi_o),
+                    *objs, "-o", str(exe)], check=True, capture_output=True)
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=1")
     r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120, env=env)
     assert r.returncode == 0, r.stdout + r.stderr

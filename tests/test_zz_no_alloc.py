@@ -122,3 +122,33 @@ def test_noalloc_refuses_inputs_beyond_its_buffer():
     ct = _sub(c, 100)
     ref, out, _, _ = _run_both(E, ct)
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
+
+
+@pytest.mark.parametrize("wfmt,T,dim,hc", [("mxfp8", 16, 1024, 3), ("bf16", 300, 512, 2)])
+def test_noalloc_forward_under_graph_capture(wfmt, T, dim, hc):
+    """The callers it is for: a forward captured into a HIP graph with no
+    allocation inside the capture. The captured engram_forward_noalloc is
+    replayed four times, with eager work and synchronizations between the
+    replays, and every replay gives the eager call's output bit for bit."""
+    E = _E()
+    c = _case(wfmt, T, dim, hc, seed=8200 + T + dim)
+    args = (c["table"], c["ids"], c["w"], c["ws"], c["hidden"], c["q"], c["k"], c["mask"])
+    eager = E.forward_noalloc(*args).clone()
+    out = torch.empty_like(c["hidden"])
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        E.forward_noalloc(*args, out=out)          # warm-up on the capture stream's side
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        E.forward_noalloc(*args, out=out)
+    for i in range(4):
+        out.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), i
+        _ = (c["hidden"].float() * 2).sum().item()   # eager work between replays
