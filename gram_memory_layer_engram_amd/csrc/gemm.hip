@@ -40,9 +40,10 @@
 //    publishes slice d+1 sits after the first 4 of the last 16 MFMAs of
 //    slice d, and the next slice's first fragments are read under the other
 //    12.
-//  * MXFP8 (K % 512 == 0, K <= 3584): two buffers of 128-e4m3 slices
-//    (gemm_mx_paced_kernel, described above it). Other K: a plain two-stage
-//    kernel with 128-byte k stages (piece p of row r at p ^ ((r >> 1) & 7)).
+//  * MXFP8 (K % 256 == 0): the same ring of five 32 KiB chunks, a slice
+//    being 128 e4m3 per row (gemm_mx_ring_kernel, described above it).
+//    Other K: a plain two-stage kernel with 128-byte k stages (piece p of
+//    row r at p ^ ((r >> 1) & 7)).
 //  * Epilogue: the bf16 tile is staged in LDS as [token][n] (512-byte rows,
 //    16-byte chunks XOR-swizzled by token) and written back as whole rows,
 //    16 bytes per lane: 8 full cache lines per store instruction instead of
@@ -524,35 +525,29 @@ void gemm_mxfp8_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict
   store_tile(acc, smem, kv, T, N, t0, n0, wn, wt, lane, wave, ep);
 }
 
-// Paced MXFP8 GEMM on the 32x32x64 scaled MFMA. A k stage is 64 e4m3 per
-// row, exactly one MFMA k step (16 MFMAs per wave); two stages form a slice
-// of 128-byte LDS rows, so a DMA instruction fetches 8 rows x 128 bytes, 8
-// whole cache lines (with one 64-byte stage per buffer and four buffers it
-// touched half of 16 lines: long-prefill GEMM 3491 -> 3395 us, prefill
-// shape ~400 -> ~381 us). Two slice buffers of 64 KiB: during a slice's
-// first stage the 16 DMAs of the next slice go out, four per quarter, and
-// the barrier that publishes it sits after the first 12 MFMAs of the second
-// stage (~37% of a slice of lead). Lane (row l%32, group g = l/32) reads,
-// for the slice's stage h, pieces 4h+g and 4h+2+g of its row (k bytes 16g..
-// and 32+16g.. of the stage) and passes the E8M0 byte of k block
-// 2*stage + g. All of the tile's scale bytes are staged in LDS once, before
-// the first stage: W's 8 block rows and x's 256 token rows are contiguous in
-// their [rows, K/32] arrays. Per stage: A fragments stream one row block
-// ahead (two register sets); B fragments, A row 0 and the scale bytes of the
-// next stage are read under the last 4 MFMAs (after the barrier when the
-// next stage opens a new slice).
-constexpr int S_ROW = 128;                      // paced MXFP8: 128-byte slices (two k steps)
-constexpr int S_TILE = BM * S_ROW;              // 32 KiB
-constexpr int S_SLICE = 2 * S_TILE;             // A + B, two slice buffers = LDS_BYTES
-static_assert(2 * S_SLICE == LDS_BYTES, "MXFP8 slice buffers");
-constexpr int MX_SCALE_A = LDS_BYTES;           // 8 W block rows x K/32 bytes (<= 1 KiB)
-constexpr int MX_SCALE_B = LDS_BYTES + 1024;    // 256 token rows x K/32 bytes
-constexpr int MX_MAX_KB = (160 * 1024 - MX_SCALE_B) / BN;
+constexpr int S_ROW = 128;                      // MXFP8 ring: 128-byte slices (two k steps)
 
+// MXFP8 GEMM on the bf16 kernel's ring (K % 256 == 0). A slice is 128
+// e4m3 per row, two MFMA k steps ("stages", 16 MFMAs per wave each), so a
+// DMA instruction fetches 8 rows x 128 bytes, 8 whole cache lines. Each
+// operand's slice is a 32 KiB chunk in a ring of five (all 160 KiB of LDS),
+// chunk c in slot c % 5 with A_d = chunk 2d and B_d = chunk 2d+1. During
+// slice d, B_{d+1} goes out in stage 0 (two DMAs per quarter) and A_{d+2} in
+// stage 1 (3, 3, 2), into the slots of A_{d-1} and B_{d-1}; the barrier that
+// publishes slice d+1 sits after three of stage 1's four MFMA row blocks.
+// A's DMAs thus get more than a slice of lead (two 64 KiB slice buffers
+// gave every DMA about 37% of one: long-prefill GEMM 3.32 -> 3.16 ms).
+// With LDS full, the E8M0 bytes are read from memory into registers, one
+// group of four stages (8 bytes per row) ahead, issued at the start of a
+// group's first slice, before its DMAs, so the barrier's wait covers them.
+// Lane (row l%32, group g = l/32) reads, for stage h, pieces 4h+g and
+// 4h+2+g of its row and passes the E8M0 byte of k block 2*stage + g. The
+// fragments stream one A row block ahead (two register sets); B and the
+// next stage's first A block are read under a stage's last four MFMAs.
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_mx_paced_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, int T, int K,
-                          const uint8_t* __restrict__ w, const uint8_t* __restrict__ ws, int N,
-                          uint16_t* __restrict__ kv, int tiles_n, int tiles_t, GateEpi ep) {
+void gemm_mx_ring_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restrict__ xs, int T, int K,
+                         const uint8_t* __restrict__ w, const uint8_t* __restrict__ ws, int N,
+                         uint16_t* __restrict__ kv, int tiles_n, int tiles_t, GateEpi ep) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   int tn, tt;
   tile_of(blockIdx.x, tiles_n, tiles_t, tn, tt);
@@ -564,37 +559,44 @@ void gemm_mx_paced_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restr
   const rsrc_t ra = make_rsrc(w + (int64_t)n0 * K, (uint32_t)min(BM, N - n0) * row_bytes);
   const rsrc_t rb = make_rsrc(xq + (int64_t)t0 * K, (uint32_t)min(BN, T - t0) * row_bytes);
   const uint32_t oob = (uint32_t)BM * row_bytes;   // at or past both ranges
-  const int nk = K / 64;
-  const int kb = K / 32;                            // scale bytes per row, a multiple of 16
+  const int ns = K / 128;                           // slices, even
+  const int kb = K / 32;                            // scale bytes per row, a multiple of 8
+  const int lrow = lane & 31, lg = lane >> 5;
 
-  // the tile's scale bytes: W block rows n0/32 .. +8 (one DMA, wave 0; lanes
-  // past the range read zeros into the rest of the 1 KiB slot), x rows t0 ..
-  // t0+256 (kb/4 DMAs of 1 KiB over the waves); issued before the stages, so
-  // the prologue's wait covers them
-  {
-    const int nb0 = n0 / 32;
-    const rsrc_t rsa = make_rsrc(ws + (int64_t)nb0 * kb, (uint32_t)(min(8, N / 32 - nb0) * kb));
-    const rsrc_t rsb = make_rsrc(xs + (int64_t)t0 * kb, (uint32_t)(min(BN, T - t0) * kb));
-    if (wave == 0)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsa, (lds_ptr_t)(smem + MX_SCALE_A), 16, (uint32_t)lane * 16u,
-                                               0, 0, 0);
-    for (int i = wave; i < kb / 4; i += 4)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsb, (lds_ptr_t)(smem + MX_SCALE_B + i * 1024), 16,
-                                               (uint32_t)(i * 1024 + lane * 16), 0, 0, 0);
-  }
-
-  // A slice is two MFMA k steps (128 e4m3 per row, 128-byte LDS rows of 8
-  // pieces, piece p of row r at p ^ ((r >> 1) & 7)); two slice buffers of
-  // 64 KiB (A then B). DMA j (0..15) of a slice: operand B for j < 8, then A;
-  // i = j % 8 fills LDS rows 8*(wave + 4i) .. +8 (gemm_dma.h), the whole
-  // offset in the range-checked vector offset.
   const dma::Lane dl = dma::lane_of(wave, lane, row_bytes);
-  auto dma = [&](int buf, uint32_t kofs, int j) {
-    const int i = j & 7, op = j < 8 ? 1 : 0;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? rb : ra,
-                                             (lds_ptr_t)(smem + buf * S_SLICE + op * S_TILE +
-                                                         (wave + 4 * i) * 1024),
+  auto dma = [&](int slot_ofs, int op, uint32_t kofs, int i) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(op ? rb : ra, (lds_ptr_t)(smem + slot_ofs + (wave + 4 * i) * 1024),
                                              16, dma::voffset(dl, i, kofs, row_bytes, oob, false), 0, 0, 0);
+  };
+
+  // The 8 scale bytes of stages s4 .. s4+3 (s4 % 4 == 0) of each row, as
+  // range-checked vector loads: a scalar load would be waited for by the
+  // next fragment read's lgkmcnt(0). Token rows past T read zeros.
+  const rsrc_t rsa = make_rsrc(ws, (uint32_t)(N / 32) * (uint32_t)kb);
+  const rsrc_t rsb = make_rsrc(xs + (int64_t)t0 * kb, (uint32_t)min(BN, T - t0) * (uint32_t)kb);
+  uint32_t arow[4], brow[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    arow[i] = (uint32_t)min((n0 + wn + i * 32) / 32, N / 32 - 1) * (uint32_t)kb;
+    brow[i] = (uint32_t)(wt + i * 32 + lrow) * (uint32_t)kb;
+  }
+  auto scales8 = [&](int s4, u32x2 (&a8)[4], u32x2 (&b8)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a8[i] = __builtin_amdgcn_raw_buffer_load_b64(rsa, arow[i] + 2u * (uint32_t)s4, 0, 0);
+      b8[i] = __builtin_amdgcn_raw_buffer_load_b64(rsb, brow[i] + 2u * (uint32_t)s4, 0, 0);
+    }
+  };
+  const uint32_t lsh = (uint32_t)lg * 8u;
+  auto pick = [&](const u32x2& v, int u) {   // u static: byte 2u + lg
+    return (int)(((u < 2 ? v.x : v.y) >> ((uint32_t)(16 * (u & 1)) + lsh)) & 0xffu);
+  };
+  auto frag = [&](int slot_ofs, int half, int row) {
+    const char* base = smem + slot_ofs + row * S_ROW;
+    const int sw = (row >> 1) & 7;
+    const i32x4 lo = *reinterpret_cast<const i32x4*>(base + (((4 * half + lg) ^ sw) << 4));
+    const i32x4 hi = *reinterpret_cast<const i32x4*>(base + (((4 * half + 2 + lg) ^ sw) << 4));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
 
   f32x16 acc[4][4];
@@ -605,33 +607,7 @@ void gemm_mx_paced_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restr
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  const int lrow = lane & 31, lg = lane >> 5;
-  // LDS reads as vector types: read through the 16-byte struct type, the
-  // compiler could not tell them from the DMAs still writing LDS and waited
-  // for every one of them (vmcnt(0)) before each read
-  auto frag = [&](int buf, int half, int op, int row) {
-    const char* base = smem + buf * S_SLICE + op * S_TILE + row * S_ROW;
-    const int sw = (row >> 1) & 7;
-    const i32x4 lo = *reinterpret_cast<const i32x4*>(base + (((4 * half + lg) ^ sw) << 4));
-    const i32x4 hi = *reinterpret_cast<const i32x4*>(base + (((4 * half + 2 + lg) ^ sw) << 4));
-    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  };
-  // Scale bytes of 4 stages at a time: for its A row block (or B row) a lane
-  // needs byte 2*stage + lg of the row's K/32; the 8 bytes of stages 4g ..
-  // 4g+3 are one 8-byte LDS read, from which stage 4g+u takes byte 2u + lg.
-  auto scales8 = [&](int kt4, u32x2 (&sa8)[4], u32x2 (&sb8)[4]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      sa8[i] = *reinterpret_cast<const u32x2*>(smem + MX_SCALE_A + ((wn >> 5) + i) * kb + kt4 * 2);
-      sb8[i] = *reinterpret_cast<const u32x2*>(smem + MX_SCALE_B + (wt + i * 32 + lrow) * kb + kt4 * 2);
-    }
-  };
-  const uint32_t lsh = (uint32_t)lg * 8u;
-  auto pick = [&](const u32x2& v, int u) {   // u static: byte 2u + lg
-    return (int)(((u < 2 ? v.x : v.y) >> ((uint32_t)(16 * (u & 1)) + lsh)) & 0xffu);
-  };
-
-  i32x8 a0, a1, b[4];
+  i32x8 a0, a1, b[4], nb[4];
   int sa[4], sb[4];
   auto mfma_row = [&](const i32x8& a, int i) {
 #pragma unroll
@@ -640,106 +616,116 @@ void gemm_mx_paced_kernel(const uint8_t* __restrict__ xq, const uint8_t* __restr
                                                                  sb[j]);
   };
 
-  // prologue: slice 0 into buffer 0
-#pragma unroll
-  for (int j = 0; j < 16; ++j) dma(0, 0u, j);
-  wait_vm<0>();
-  bare_barrier();
-  u32x2 sa8[4], sb8[4];
+  // prologue: the first group's scale bytes, then A_0 -> slot 0, B_0 -> slot
+  // 1, A_1 -> slot 2; wait for all but A_1's 8 DMAs
+  u32x2 sa8[4], sb8[4], na8[4], nb8[4];
   scales8(0, sa8, sb8);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int j = 0; j < 4; ++j) b[j] = frag(0, 0, 1, wt + j * 32 + lrow);
-  a0 = frag(0, 0, 0, wn + lrow);
+  for (int i = 0; i < Q_DMA; ++i) dma(0, 0, 0u, i);
+#pragma unroll
+  for (int i = 0; i < Q_DMA; ++i) dma(Q_CHUNK, 1, 0u, i);
+#pragma unroll
+  for (int i = 0; i < Q_DMA; ++i) dma(2 * Q_CHUNK, 0, ns > 1 ? (uint32_t)S_ROW : oob, i);
+  wait_vm<Q_DMA>();
+  // a use here keeps the first group's scale loads ahead of the DMAs (left
+  // to itself, the compiler sinks them to the loop, and the waits it then
+  // places at the loop head drain every slice's DMAs)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) asm volatile("" : "+v"(sa8[i]), "+v"(sb8[i]));
+  bare_barrier();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) b[j] = frag(Q_CHUNK, 0, wt + j * 32 + lrow);
+  a0 = frag(0, 0, wn + lrow);
 
-  // nk % 4 == 0 (K % 512 == 0): groups of four stages = two slices, so
-  // every buffer index below is a constant. Stage kt is half kt % 2 of slice
-  // kt / 2; in a slice's first half the 16 DMAs of the next slice go out
-  // (four per quarter, into the other buffer, free since the last barrier),
-  // and the barrier that publishes it sits in the second half.
-  for (int kt4 = 0; kt4 < nk; kt4 += 4) {
-    u32x2 na8[4], nb8[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int kt = kt4 + u;
-      const int half = u & 1, cur = u >> 1;
-      const int nbuf = half ? cur ^ 1 : cur, nhalf = half ^ 1;   // buffer and half of stage kt+1
-      const uint32_t kofs = (kt >> 1) + 1 < nk / 2 ? (uint32_t)((kt >> 1) + 1) * S_ROW : oob;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        sa[i] = pick(sa8[i], u);
-        sb[i] = pick(sb8[i], u);
-      }
-      // quarters 0, 1: the next A row blocks, 4 MFMAs each (first half: 4 DMAs each)
-      __builtin_amdgcn_sched_barrier(0);
-      if (!half) { dma(cur ^ 1, kofs, 0); dma(cur ^ 1, kofs, 1); dma(cur ^ 1, kofs, 2); dma(cur ^ 1, kofs, 3); }
-      a1 = frag(cur, half, 0, wn + 32 + lrow);
-      mfma_row(a0, 0);
-      if (!half) {
-        SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 1);
-        SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1);
-      } else {
-        SGB(SG_MFMA, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 2);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      if (!half) { dma(cur ^ 1, kofs, 4); dma(cur ^ 1, kofs, 5); dma(cur ^ 1, kofs, 6); dma(cur ^ 1, kofs, 7); }
-      a0 = frag(cur, half, 0, wn + 64 + lrow);
-      mfma_row(a1, 1);
-      if (!half) {
-        SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 1);
-        SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1);
-      } else {
-        SGB(SG_MFMA, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 2);
-      }
-      // quarter 2: the last A row block of this stage; in a second half, then
-      // publish the next slice: each wave waits for all of its DMAs and its
-      // LDS reads, then the barrier
-      __builtin_amdgcn_sched_barrier(0);
-      if (!half) { dma(cur ^ 1, kofs, 8); dma(cur ^ 1, kofs, 9); dma(cur ^ 1, kofs, 10); dma(cur ^ 1, kofs, 11); }
-      a1 = frag(cur, half, 0, wn + 96 + lrow);
-      mfma_row(a0, 2);
-      if (!half) {
-        SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 1);
-        SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1);
-      } else {
-        SGB(SG_MFMA, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 2);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      if (half) {
-        wait_vm<0>();
-        wait_lgkm0();
-        bare_barrier();
-      }
-      // quarter 3: stage kt+1's B fragments and A row block 0 (and, closing a
-      // group, the next group's scale bytes) under the last 4 MFMAs
-      __builtin_amdgcn_sched_barrier(0);
-      if (!half) { dma(cur ^ 1, kofs, 12); dma(cur ^ 1, kofs, 13); dma(cur ^ 1, kofs, 14); dma(cur ^ 1, kofs, 15); }
-      i32x8 nb[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) nb[j] = frag(nbuf, nhalf, 1, wt + j * 32 + lrow);
-      a0 = frag(nbuf, nhalf, 0, wn + lrow);
-      if (u == 3) scales8(min(kt4 + 4, nk - 4), na8, nb8);   // the last group reloads itself, unused
-      mfma_row(a1, 3);
-      if (u == 3) {
-        SGB(SG_MFMA, 1); SGB(SG_DSR, 6); SGB(SG_MFMA, 1); SGB(SG_DSR, 6); SGB(SG_MFMA, 1); SGB(SG_DSR, 6);
-        SGB(SG_MFMA, 1);
-      } else if (!half) {
-        SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 4); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1);
-        SGB(SG_DSR, 3); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 3); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1);
-      } else {
-        SGB(SG_MFMA, 1); SGB(SG_DSR, 4); SGB(SG_MFMA, 1); SGB(SG_DSR, 3); SGB(SG_MFMA, 1); SGB(SG_DSR, 3);
-        SGB(SG_MFMA, 1);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = nb[j];
-    }
+  int base = 0;   // (2d) % 5
+  // one slice; PAR = d % 2 (the slice's place in its group of two)
+  auto slice = [&](int d, auto par) {
+    constexpr int PAR = decltype(par)::value;
+    auto slot = [&](int m) { const int v = base + m; return (v >= Q_SLOTS ? v - Q_SLOTS : v) * Q_CHUNK; };
+    const int s_a = slot(0), s_b = slot(1), s_a1 = slot(2), s_b1 = slot(3), s_a2 = slot(4);
+    const uint32_t kb1 = d + 1 < ns ? (uint32_t)(d + 1) * S_ROW : oob;
+    const uint32_t ka2 = d + 2 < ns ? (uint32_t)(d + 2) * S_ROW : oob;
+    if (PAR == 0) scales8(min(2 * d + 4, 2 * ns - 4), na8, nb8);   // the last group reloads itself, unused
+    // stage 0: B_{d+1}, two DMAs per quarter
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      sa8[i] = na8[i];
-      sb8[i] = nb8[i];
+      sa[i] = pick(sa8[i], 2 * PAR);
+      sb[i] = pick(sb8[i], 2 * PAR);
     }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      __builtin_amdgcn_sched_barrier(0);
+      dma(s_b1, 1, kb1, 2 * q);
+      dma(s_b1, 1, kb1, 2 * q + 1);
+      if (q < 3) {
+        if (q & 1) a0 = frag(s_a, 0, wn + (q + 1) * 32 + lrow);
+        else a1 = frag(s_a, 0, wn + (q + 1) * 32 + lrow);
+        mfma_row((q & 1) ? a1 : a0, q);
+        SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 1);
+        SGB(SG_MFMA, 2);
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) nb[j] = frag(s_b, 1, wt + j * 32 + lrow);
+        a0 = frag(s_a, 1, wn + lrow);
+        mfma_row(a1, 3);
+        SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 4); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 3);
+        SGB(SG_MFMA, 1); SGB(SG_DSR, 3); SGB(SG_MFMA, 1);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = nb[j];
+    // stage 1: A_{d+2}, 3 + 3 + 2 DMAs; the barrier after the third row block
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sa[i] = pick(sa8[i], 2 * PAR + 1);
+      sb[i] = pick(sb8[i], 2 * PAR + 1);
+    }
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      __builtin_amdgcn_sched_barrier(0);
+      const int nd = q < 2 ? 3 : 2, d0 = 3 * q;
+#pragma unroll
+      for (int k = 0; k < nd; ++k) dma(s_a2, 0, ka2, d0 + k);
+      if (q & 1) a0 = frag(s_a, 1, wn + (q + 1) * 32 + lrow);
+      else a1 = frag(s_a, 1, wn + (q + 1) * 32 + lrow);
+      mfma_row((q & 1) ? a1 : a0, q);
+      if (nd == 3) {
+        SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 1);
+        SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_MFMA, 1);
+      } else {
+        SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 1); SGB(SG_MFMA, 1); SGB(SG_VMEM, 1); SGB(SG_DSR, 1);
+        SGB(SG_MFMA, 2);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<Q_DMA>();   // all but A_{d+2}'s 8: B_{d+1}, A_{d+1} and the scale loads are in
+    wait_lgkm0();
+    bare_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) nb[j] = frag(s_b1, 0, wt + j * 32 + lrow);
+    a0 = frag(s_a1, 0, wn + lrow);
+    mfma_row(a1, 3);
+    SGB(SG_MFMA, 1); SGB(SG_DSR, 4); SGB(SG_MFMA, 1); SGB(SG_DSR, 3); SGB(SG_MFMA, 1); SGB(SG_DSR, 3);
+    SGB(SG_MFMA, 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = nb[j];
+    if (PAR == 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sa8[i] = na8[i];
+        sb8[i] = nb8[i];
+      }
+    }
+    base = base + 2 >= Q_SLOTS ? base + 2 - Q_SLOTS : base + 2;
+  };
+  for (int d = 0; d < ns; d += 2) {
+    slice(d, std::integral_constant<int, 0>{});
+    slice(d + 1, std::integral_constant<int, 1>{});
   }
   __builtin_amdgcn_sched_barrier(0);
-  wait_vm<0>();   // the zero-fill DMAs of the last stages land before LDS is reused
+  wait_vm<0>();   // the zero-fill DMAs of the last slices land before LDS is reused
   store_tile(acc, smem, kv, T, N, t0, n0, wn, wt, lane, wave, ep);
 }
 
@@ -771,14 +757,11 @@ hipError_t launch_gemm_mxfp8(const uint8_t* xq, const uint8_t* xs, int64_t T, in
                              const uint8_t* ws, int N, void* kv, hipStream_t s, const GateEpi& ep) {
   const int tiles_n = (N + BM - 1) / BM;
   const int tiles_t = (int)((T + BN - 1) / BN);
-  if (K % 512 == 0 && K / 32 <= MX_MAX_KB && N % 32 == 0) {
-    // the paced kernel: 16-byte pieces of scale rows, the tile's scales in LDS
-    const int lds = MX_SCALE_B + BN * (K / 32);
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_mx_paced_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (K % 256 == 0 && N % 32 == 0) {
+    hipError_t e = set_lds((const void*)gemm_mx_ring_kernel, Q_LDS);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(gemm_mx_paced_kernel, dim3(tiles_n * tiles_t), dim3(THREADS), lds, s, xq, xs,
-                       (int)T, K, w, ws, N, (uint16_t*)kv, tiles_n, tiles_t, ep);
+    hipLaunchKernelGGL(gemm_mx_ring_kernel, dim3(tiles_n * tiles_t), dim3(THREADS), Q_LDS, s, xq, xs, (int)T,
+                       K, w, ws, N, (uint16_t*)kv, tiles_n, tiles_t, ep);
     return hipGetLastError();
   }
   hipError_t e = set_lds((const void*)gemm_mxfp8_kernel);

@@ -579,7 +579,10 @@ def test_wkv(name):
                                    (33, 264, 100), (257, 72, 260), (1, 8, 4),
                                    (40, 96, 264), (3, 32, 512), (130, 160, 132),
                                    # one and two whole k slices
-                                   (5, 64, 256), (70, 128, 136)])
+                                   (5, 64, 256), (70, 128, 136),
+                                   # MXFP8 GEMM with K % 512 == 256 (an odd number of
+                                   # 256-wide k groups) and with a single group, N < 256
+                                   (100, 768, 352), (257, 256, 64)])
 def test_wkv_ragged_shapes(fmt, T, K, N):
     E = _E()
     g = torch.Generator(device=DEV).manual_seed(T * 7 + K + N)
