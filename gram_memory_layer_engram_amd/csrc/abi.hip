@@ -1,5 +1,6 @@
 // C ABI of libengram: argument validation, workspace layout and dispatch.
-// Every entry point only enqueues work on the caller's stream.
+// Every compute entry point only enqueues work on the caller's stream
+// (engram_host_alloc / engram_host_free manage host memory and block).
 #include "../../include/engram.h"
 #include <algorithm>
 #include <mutex>
@@ -10,11 +11,15 @@
 
 namespace engram {
 
+// Filled once per device under a lock, so calls from several host threads
+// are safe; entries never change once filled.
 const DevInfo& dev_info() {
   static DevInfo info[64];
   static bool ready[64] = {false};
+  static std::mutex mu;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  std::lock_guard<std::mutex> lock(mu);
   if (!ready[dev]) {
     int cus = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
@@ -196,6 +201,9 @@ int engram_host_alloc(size_t bytes, void** host_ptr, void** device_ptr) {
 
 int engram_host_free(void* host_ptr) {
   if (!host_ptr) return ENGRAM_OK;
+  // kernels enqueued earlier may still read the memory: let the current
+  // device drain before it goes back to the host
+  if (hipDeviceSynchronize() != hipSuccess) return ENGRAM_EHIP;
   return hip_status(hipHostFree(host_ptr));
 }
 

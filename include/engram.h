@@ -110,6 +110,10 @@ int engram_lookup_background(const void* table, int64_t num_rows, int32_t head_d
  *                  host link (results bit for bit those of a device table).
  *   The memory is the caller's until engram_host_free(host_ptr); it is not
  *   a device allocation and is never touched by the library otherwise.
+ *   engram_host_free first waits for all work on the current device to
+ *   finish (hipDeviceSynchronize), so lookups still queued there cannot
+ *   read freed memory; work on other devices that reads it must be
+ *   finished by the caller. It is not allowed during stream capture.
  *   ENGRAM_EINVAL for bytes == 0 or NULL out-pointers, ENGRAM_EHIP when the
  *   runtime cannot allocate or map it (both out-pointers are then NULL).
  *   engram_host_free(NULL) is a no-op.
