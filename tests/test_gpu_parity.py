@@ -302,6 +302,26 @@ def test_host_table_lookup_and_forward(wfmt, T):
         ht.close()
 
 
+def test_host_table_free_waits_for_queued_gathers():
+    """engram_host_free drains the device before the memory goes back: a
+    gather of 64K rows over the host link (a few hundred microseconds) is
+    enqueued and the table freed right after, with no synchronization in
+    between; the rows are still the table's."""
+    E = _E()
+    g = torch.Generator(device=DEV).manual_seed(7411)
+    R, T, C, hd = 200003, 4096, 16, 128
+    table = (torch.randn((R, hd), generator=g, device=DEV) * 0.02).to(torch.bfloat16)
+    ids = torch.randint(0, R, (T, C), generator=g, device=DEV, dtype=torch.int32)
+    want = E.lookup(table, ids)
+    _say("host table freed behind a queued gather")
+    ht = E.HostTable(R, hd).copy_from(table)
+    rows = E.lookup(ht, ids)
+    ht.close()
+    assert ht.device_ptr is None
+    torch.cuda.synchronize()
+    assert torch.equal(rows.view(torch.int16), want.view(torch.int16))
+
+
 @pytest.mark.parametrize("hd", [8, 32, 64, 128, 96, 1024])
 @pytest.mark.parametrize("T", [1, 17, 65, 1000])
 def test_lookup_shapes(hd, T):
