@@ -956,14 +956,16 @@ def test_forward_gate_epilogue_and_plain_paths(wfmt, T, dim, hc):
 
 @pytest.mark.parametrize("wfmt,T,dim,hc,K", [("bf16", 300, 512, 2, 512), ("bf16", 1, 256, 1, 512),
                                              ("mxfp8", 257, 1024, 3, 512), ("mxfp8", 17, 256, 2, 512),
-                                             ("bf16", 130, 256, 2, 520), ("mxfp8", 100, 512, 2, 384)])
+                                             ("bf16", 130, 256, 2, 520), ("mxfp8", 100, 512, 2, 384),
+                                             ("mxfp8", 300, 512, 2, 768)])
 def test_wkv_gate_partials_against_oracle_partials(wfmt, T, dim, hc, K):
     """engram_wkv_gate_partials: the value block and, per 256-column key
     tile, (sum hidden*q*k*key, sum key^2) against the oracle's partial sums
     (the shard route of the gate) taken on the same bf16 keys, which the
     plain projection stores; the value is bit-identical to that projection's
     where both run the tiled GEMM. K = 520 takes the bf16 kernel's ragged
-    last k-stage, K = 384 the MXFP8 kernel for K % 512 != 0."""
+    last k-stage, K = 384 the plain MXFP8 kernel (K % 256 != 0), K = 768 the
+    MXFP8 ring kernel with an odd number of 256-wide k groups."""
     E = _E()
     g = torch.Generator(device=DEV).manual_seed(4000 + T + dim + K)
     N = (hc + 1) * dim
