@@ -12,7 +12,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libengram.so")
-SOURCES = ["abi.hip", "lookup.hip", "gate.hip", "mxq.hip", "gemm.hip", "gemv_mxfp8.hip", "decode_forward.hip",
+SOURCES = ["abi.hip", "lookup.hip", "gate.hip", "mxq.hip", "gemm.hip", "gemv_mxfp8.hip", "gemv_bf16.hip", "decode_forward.hip",
            "probe.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

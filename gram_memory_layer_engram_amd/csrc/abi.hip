@@ -84,7 +84,8 @@ int run_wkv(const void* x, int64_t T, int32_t K, const void* w,
             void* workspace, hipStream_t s, const GateEpi& ep = kPlainStore) {
   if (T == 0) return ENGRAM_OK;
   if (w_format == ENGRAM_W_BF16)
-    return hip_status(launch_gemm_bf16(x, T, K, w, N, kv, s, ep));
+    return hip_status(!ep.hidden && gemv_bf16_supported(T, K, N) ? launch_gemv_bf16(x, T, K, w, N, kv, s)
+                                                                 : launch_gemm_bf16(x, T, K, w, N, kv, s, ep));
   uint8_t* xq = (uint8_t*)workspace;
   uint8_t* xs = xq + round_up((size_t)T * K);
   hipError_t e = launch_mx_quantize(x, T, K, xq, xs, s);
@@ -357,7 +358,8 @@ static int run_forward(const engram_forward_args* a, int32_t K, int32_t N, uint8
   // turns key tiles into the gate's partial sums and stores only the value:
   // kv's keys never reach HBM. The value and partials take kv's place in the
   // workspace.
-  const bool tiled = a->w_format == ENGRAM_W_BF16 || !gemv_mxfp8_supported(a->T, K);
+  const bool tiled = a->w_format == ENGRAM_W_BF16 ? !gemv_bf16_supported(a->T, K, N)
+                                                 : !gemv_mxfp8_supported(a->T, K);
   const bool epi = !(a->options & ENGRAM_FORWARD_STORE_KV) && tiled && a->dim % 256 == 0;
   uint16_t* value = (uint16_t*)kv;
   float2* part = (float2*)((uint8_t*)kv + round_up((size_t)a->T * a->dim * 2));

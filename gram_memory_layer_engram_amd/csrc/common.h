@@ -107,6 +107,11 @@ hipError_t launch_gemv_mxfp8(const uint8_t* xq, const uint8_t* xs, int64_t T,
 // Largest T the decode GEMV serves; above it the tiled GEMM runs.
 constexpr int kGemvMaxT = 64;
 
+// Small-batch projection with bf16 weights (T <= kGemvMaxT): whether the
+// weight-streaming GEMV takes (T, K, N), and its launch (plain kv store).
+bool gemv_bf16_supported(int64_t T, int K, int N);
+hipError_t launch_gemv_bf16(const void* x, int64_t T, int K, const void* w, int N, void* kv, hipStream_t s);
+
 // Whether the decode GEMV takes (T, K): T <= kGemvMaxT and K small enough for
 // its per-wave register budget.
 bool gemv_mxfp8_supported(int64_t T, int K);

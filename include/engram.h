@@ -178,6 +178,10 @@ int engram_mx_quantize(const void* x, int64_t T, int32_t K, uint8_t* xq,
  *   Shapes: bf16 needs K % 8 == 0 and N % 4 == 0; MXFP8 needs K % 128 == 0
  *   and N % 32 == 0; both need K <= 2^20 (32-bit buffer offsets). Other
  *   shapes return ENGRAM_EUNSUPPORTED.
+ *   Kernels: a tiled GEMM; for T <= 64 a weight-streaming GEMV instead
+ *   (MXFP8 with K/128 <= 32; bf16 with K % 32 == 0, K <= 2048, N % 16 == 0
+ *   where it beats the GEMM). The two sum in different fp32 orders, so
+ *   their kv can differ in the last bit.
  */
 size_t engram_wkv_workspace_size(int64_t T, int32_t K, int32_t N,
                                  int32_t w_format);
@@ -208,8 +212,8 @@ int engram_wkv(const void* x, int64_t T, int32_t K, const void* w,
  *   Errors: ENGRAM_EINVAL for hc or dim <= 0, a NULL or misaligned pointer,
  *   or a short workspace; T = 0 is a no-op. Asynchronous on `stream`.
  *   Shapes: as engram_wkv, plus dim % 256 == 0 and 1 <= hc <= 8; other
- *   shapes return ENGRAM_EUNSUPPORTED. MXFP8 always runs the tiled GEMM
- *   here (engram_wkv would take the decode GEMV for T <= 64).
+ *   shapes return ENGRAM_EUNSUPPORTED. This always runs the tiled GEMM
+ *   (engram_wkv may take a GEMV for T <= 64).
  */
 int engram_wkv_gate_partials(const void* x, int64_t T, int32_t K, const void* w,
                              const uint8_t* w_scales, int32_t w_format, int32_t hc,
@@ -316,8 +320,8 @@ typedef struct engram_forward_args {
 
 /*
  * Gate epilogue (the default) and ENGRAM_FORWARD_STORE_KV. Where the
- *   projection runs as a tiled GEMM (bf16 weights, or MXFP8 with T too large
- *   for the decode GEMV) and dim % 256 == 0, engram_forward by default has
+ *   projection runs as a tiled GEMM (T too large for the GEMV of engram_wkv,
+ *   or a shape it does not take) and dim % 256 == 0, engram_forward by default has
  *   the GEMM's epilogue reduce each 256-column key tile against hidden, q
  *   and k to the gate's per-tile sums (sum key^2, sum hidden*q*k*key over the
  *   bf16-rounded keys: the partial / finish split of [P-rocm]

@@ -17,12 +17,15 @@ import subprocess
 
 import pytest
 
+from gram_memory_layer_engram_amd import build as BUILD
+
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 PKG = os.path.join(ROOT, "gram_memory_layer_engram_amd")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 
-OTHERS = ["lookup", "gate", "mxq", "gemm", "gemv_mxfp8", "decode_forward", "probe"]
+# every other object the library links (the build's source list, less abi.hip)
+OTHERS = [s[:-len(".hip")] for s in BUILD.SOURCES if s != "abi.hip"]
 
 
 def test_abi_checks_under_asan(tmp_path):

@@ -96,8 +96,8 @@ ALL = ["tiny", "mid", "prefill", "decode_t1", "decode_t4", "decode_t16", "decode
 
 def own_kv_rows(E, inp, toks):
     """kv of the sampled tokens as the GPU's own projection forms it:
-    engram_lookup + engram_wkv over all tokens (the tiled GEMM, or the decode
-    GEMV for MXFP8 at T <= 64), the kernels and operand bits every forward
+    engram_lookup + engram_wkv over all tokens (the tiled GEMM, or the
+    weight-streaming GEMV at T <= 64), the kernels and operand bits every forward
     route runs on (the fused gather + MX quantize gives the same codes as
     lookup + engram_mx_quantize). Rows of the sampled tokens, as bf16 bits."""
     wl = inp["wl"]
@@ -963,7 +963,8 @@ def test_wkv_gate_partials_against_oracle_partials(wfmt, T, dim, hc, K):
     tile, (sum hidden*q*k*key, sum key^2) against the oracle's partial sums
     (the shard route of the gate) taken on the same bf16 keys, which the
     plain projection stores; the value is bit-identical to that projection's
-    where both run the tiled GEMM. K = 520 takes the bf16 kernel's ragged
+    where both run the tiled GEMM (T > 64; below it engram_wkv runs the
+    weight-streaming GEMV, bf16 or MXFP8). K = 520 takes the bf16 kernel's ragged
     last k-stage, K = 384 the plain MXFP8 kernel (K % 256 != 0), K = 768 the
     MXFP8 ring kernel with an odd number of 256-wide k groups."""
     E = _E()
@@ -983,11 +984,11 @@ def test_wkv_gate_partials_against_oracle_partials(wfmt, T, dim, hc, K):
     kv = E.wkv(x, w, ws)
     torch.cuda.synchronize()
     kvb = bits(kv)
-    tiled = wfmt == "bf16" or T > 64   # engram_wkv runs the tiled GEMM too
+    tiled = T > 64   # engram_wkv runs the tiled GEMM too (at T <= 64, a GEMV)
     if tiled:
         assert np.array_equal(bits(value), kvb[:, hc * dim:])
     else:
-        ref, _ = o.wkv(bits(x), u8(w), u8(ws))
+        ref, _ = o.wkv(bits(x), bits(w) if ws is None else u8(w), None if ws is None else u8(ws))
         assert_close(bf16_values(bits(value)), bf16_values(ref[:, hc * dim:]), *KV_TOL, what="value")
     p = part.cpu().numpy()
     hb, qb, kb = bits(hidden), bits(q), bits(k)
