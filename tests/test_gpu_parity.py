@@ -602,7 +602,10 @@ def test_wkv(name):
                                    (5, 64, 256), (70, 128, 136),
                                    # MXFP8 GEMM with K % 512 == 256 (an odd number of
                                    # 256-wide k groups) and with a single group, N < 256
-                                   (100, 768, 352), (257, 256, 64)])
+                                   (100, 768, 352), (257, 256, 64),
+                                   # the GEMVs (T <= 64) at 8 / 4 k steps per wave and
+                                   # 1, 2, 3 token tiles
+                                   (16, 2048, 2560), (20, 1024, 640), (40, 2048, 1280)])
 def test_wkv_ragged_shapes(fmt, T, K, N):
     E = _E()
     g = torch.Generator(device=DEV).manual_seed(T * 7 + K + N)
