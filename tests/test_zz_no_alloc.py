@@ -78,6 +78,7 @@ def _run_both(E, c, store_kv=False):
     ("bf16", 300, 70, 512, 2, False),      # GEMM with the gate epilogue, then a smaller call
     ("bf16", 300, 70, 512, 2, True),       # kv stored, plain gate
     ("mxfp8", 64, 5, 1024, 3, False),      # fused gather + quantize, decode GEMV
+    ("bf16", 64, 9, 512, 2, False),        # bf16 weight-streaming GEMV, plain gate
     ("mxfp8", 257, 16, 512, 2, False),     # scaled GEMM (epilogue), then the decode GEMV
 ])
 def test_noalloc_forward_equals_forward(wfmt, T1, T2, dim, hc, store_kv):
@@ -124,7 +125,7 @@ def test_noalloc_refuses_inputs_beyond_its_buffer():
     assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
 
 
-@pytest.mark.parametrize("wfmt,T,dim,hc", [("mxfp8", 16, 1024, 3), ("bf16", 300, 512, 2)])
+@pytest.mark.parametrize("wfmt,T,dim,hc", [("mxfp8", 16, 1024, 3), ("bf16", 300, 512, 2), ("bf16", 16, 512, 2)])
 def test_noalloc_forward_under_graph_capture(wfmt, T, dim, hc):
     """The callers it is for: a forward captured into a HIP graph with no
     allocation inside the capture. The captured engram_forward_noalloc is
